@@ -1,0 +1,20 @@
+"""Plain fp64 CPU oracle for exact attention.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this package.
+The HIP library and its Python binding never import it, and it imports nothing
+from them.
+
+* :mod:`oracle.attention` -- the plain definition (two passes over full score
+  rows) of the forward output, the log-sum-exp statistics and the analytic
+  gradients.
+* :mod:`oracle.streaming` -- the pages' block-by-block recurrence (running max,
+  running sum, rescaled output), used only to pin the definition against the
+  method's own algorithm.
+"""
+from .attention import (allowed_mask, forward, backward, forward_rows,
+                        probabilities)
+from .streaming import merge_stats, streaming_forward
+
+__all__ = ["allowed_mask", "forward", "backward", "forward_rows",
+           "probabilities", "merge_stats", "streaming_forward"]

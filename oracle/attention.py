@@ -1,0 +1,193 @@
+"""fp64 reference for exact scaled-dot-product attention (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the product path.
+
+What is computed, and where the pages define it
+-----------------------------------------------
+* FlashAttention summary page (xyznot.com, paper 2205.14135), section
+  "Problem and motivation": S = Q K^T, P = softmax(S), O = P V.  The method is
+  exact, so the oracle is that definition written out: every score row is
+  formed in full, its maximum and exponential sum are taken in a first pass,
+  and P and O in a second pass.
+* The same page, section "Key ideas" (recomputation bullet): the forward pass
+  keeps the softmax statistics (l, m) for the backward pass.  We keep them as
+  the natural log-sum-exp of the scaled, masked score row, LSE = m + ln(l);
+  P = exp(S - LSE) recovers the probabilities from it.
+* Masking is named in the same section's kernel-fusion bullet; the
+  block-sparse section of that page defines the block mask M over row and
+  column blocks.  Readings (scale applied before masking, causal j <= i,
+  key padding j < len_b, block (i // mb, j // mb)) are listed in the design doc.
+* The gradients are not printed on the pages; they are the analytic
+  derivatives of the definition above for the loss <dO, O>:
+      dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
+      dS = P * (dP - D 1^T),  dQ = scale dS K,  dK = scale dS^T Q.
+
+Conventions: arrays are float64 numpy arrays shaped [B, H, N, d]; ``scale`` is
+applied as a float64 number (callers pass the float32 value the GPU uses); a
+query row with no visible key has O = 0, LSE = -inf and zero gradients.
+Rows are processed in chunks of ``chunk`` queries only to bound memory; each
+chunk still forms its full score rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["allowed_mask", "forward", "forward_rows", "backward", "probabilities"]
+
+
+def _block_mask_for_head(block_mask, h):
+    if block_mask is None:
+        return None
+    bm = np.asarray(block_mask)
+    if bm.ndim == 3:
+        return bm[h]
+    return bm
+
+
+def allowed_mask(rows, N, *, causal=False, key_len=None, block_mask=None, mb=128):
+    """Boolean [len(rows), N]: True where query ``rows[r]`` may see key j.
+
+    The allowed set is the AND of every active mask:
+    causal (j <= i), key padding (j < key_len) and block (M[i//mb, j//mb] != 0).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.arange(N, dtype=np.int64)
+    a = np.ones((rows.size, N), dtype=bool)
+    if causal:
+        a &= cols[None, :] <= rows[:, None]
+    if key_len is not None:
+        a &= cols[None, :] < int(key_len)
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        a &= bm[rows[:, None] // mb, cols[None, :] // mb]
+    return a
+
+
+def _row_softmax_stats(s):
+    """Two-pass statistics of masked score rows (-inf marks a masked entry).
+
+    Returns (m, l, valid): row max, sum of exp(s - m), and whether the row has
+    any visible key.
+    """
+    valid = np.isfinite(s).any(axis=1)
+    m = np.where(valid, np.max(np.where(np.isfinite(s), s, -np.inf), axis=1), 0.0)
+    e = np.exp(s - m[:, None])          # exp(-inf) = 0 for masked entries
+    l = e.sum(axis=1)
+    return m, l, valid, e
+
+
+def forward_rows(q, k, v, scale, rows, *, causal=False, key_len=None,
+                 block_mask=None, mb=128):
+    """O and LSE of one (batch, head) for the query indices ``rows`` only.
+
+    q: [N, d] (only ``rows`` are read), k, v: [N, d].  Returns (o [R, d],
+    lse [R]).  Used for sampled parity at sizes where every row is too many.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    N = k.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    s = float(scale) * (q[rows] @ k.T)
+    a = allowed_mask(rows, N, causal=causal, key_len=key_len,
+                     block_mask=block_mask, mb=mb)
+    s = np.where(a, s, -np.inf)
+    m, l, valid, e = _row_softmax_stats(s)
+    p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
+    o = p @ v
+    lse = np.where(valid, m + np.log(np.where(valid, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def _lens(key_lens, B):
+    if key_lens is None:
+        return [None] * B
+    kl = np.asarray(key_lens).reshape(-1)
+    assert kl.size == B
+    return [int(x) for x in kl]
+
+
+def forward(q, k, v, scale, *, causal=False, key_lens=None, block_mask=None,
+            mb=128, chunk=1024):
+    """Exact attention forward.  Returns (O [B,H,N,dv], LSE [B,H,N]) in fp64.
+
+    N is the number of query rows; K and V may hold a different number of
+    rows (keys), and V a different width dv.
+    """
+    B, H, N, _ = q.shape
+    o = np.zeros((B, H, N, v.shape[-1]), np.float64)
+    lse = np.zeros((B, H, N), np.float64)
+    lens = _lens(key_lens, B)
+    for b in range(B):
+        for h in range(H):
+            bm = _block_mask_for_head(block_mask, h)
+            for r0 in range(0, N, chunk):
+                rows = np.arange(r0, min(N, r0 + chunk))
+                ob, lb = forward_rows(q[b, h], k[b, h], v[b, h], scale, rows,
+                                      causal=causal, key_len=lens[b],
+                                      block_mask=bm, mb=mb)
+                o[b, h, rows] = ob
+                lse[b, h, rows] = lb
+    return o, lse
+
+
+def probabilities(q, k, scale, *, causal=False, key_len=None, block_mask=None, mb=128):
+    """P = softmax of the scaled, masked score matrix of one (batch, head): [N, N].
+
+    A row with no visible key is all zeros.  Only for small N (tests).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    N = k.shape[0]
+    rows = np.arange(q.shape[0])
+    s = float(scale) * (q @ k.T)
+    s = np.where(allowed_mask(rows, N, causal=causal, key_len=key_len,
+                              block_mask=block_mask, mb=mb), s, -np.inf)
+    m, l, valid, e = _row_softmax_stats(s)
+    return np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
+
+
+def backward(q, k, v, do, scale, *, causal=False, key_lens=None, block_mask=None,
+             mb=128, chunk=1024, return_aux=False):
+    """Analytic gradients of <dO, O> w.r.t. Q, K, V (fp64).
+
+    Returns (dq, dk, dv); with ``return_aux`` also (o, lse, D_from_p, D_from_o),
+    where D_from_p = rowsum(P * dP) and D_from_o = rowsum(dO * O) -- equal in
+    exact arithmetic; the GPU computes the latter.
+    """
+    B, H, N, d = q.shape
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk = np.zeros_like(k, dtype=np.float64)
+    dv = np.zeros_like(v, dtype=np.float64)
+    o = np.zeros((B, H, N, d), np.float64)
+    lse = np.zeros((B, H, N), np.float64)
+    D_p = np.zeros((B, H, N), np.float64)
+    D_o = np.zeros((B, H, N), np.float64)
+    lens = _lens(key_lens, B)
+    for b in range(B):
+        for h in range(H):
+            bm = _block_mask_for_head(block_mask, h)
+            qb, kb, vb, dob = (np.asarray(x[b, h], np.float64) for x in (q, k, v, do))
+            for r0 in range(0, N, chunk):
+                rows = np.arange(r0, min(N, r0 + chunk))
+                s = float(scale) * (qb[rows] @ kb.T)
+                a = allowed_mask(rows, N, causal=causal, key_len=lens[b],
+                                 block_mask=bm, mb=mb)
+                s = np.where(a, s, -np.inf)
+                m, l, valid, e = _row_softmax_stats(s)
+                p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
+                oc = p @ vb
+                dpc = dob[rows] @ vb.T
+                Dp = np.sum(p * dpc, axis=1)
+                ds = p * (dpc - Dp[:, None])
+                dq[b, h, rows] = float(scale) * (ds @ kb)
+                dk[b, h] += float(scale) * (ds.T @ qb[rows])
+                dv[b, h] += p.T @ dob[rows]
+                o[b, h, rows] = oc
+                lse[b, h, rows] = np.where(valid, m + np.log(np.where(valid, l, 1.0)), -np.inf)
+                D_p[b, h, rows] = Dp
+                D_o[b, h, rows] = np.sum(dob[rows] * oc, axis=1)
+    if return_aux:
+        return dq, dk, dv, (o, lse, D_p, D_o)
+    return dq, dk, dv
