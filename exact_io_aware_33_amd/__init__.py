@@ -1,0 +1,166 @@
+"""Exact IO-aware attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libfa.so`` (include/fa.h).  Each
+function below has the name of the C entry point it calls and only marshals
+arguments: torch supplies device memory and the current HIP stream, every step
+of the computation runs in the library's HIP kernels.  There is no fallback:
+if the library is missing, the call raises.
+
+Tensors are ``[B, H, N, d]`` views with unit stride along d; Q, K, V, O, dO
+(and the gradients this module allocates) share one set of strides.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import FaError, FaProblem
+
+__all__ = ["fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_blocksparse",
+           "fa_bwd_workspace_bytes", "FaError", "library_path", "load_library"]
+
+_DTYPES = {torch.float32: _lib.FA_DTYPE_F32, torch.float16: _lib.FA_DTYPE_F16,
+           torch.bfloat16: _lib.FA_DTYPE_BF16}
+
+
+def load_library():
+    """Load libfa.so now (raises if it was not built)."""
+    return _lib.load()
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _problem(q, scale, causal, key_lens):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, N, d = q.shape
+    if q.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous (stride 1)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or key_lens.device != q.device or key_lens.numel() != B:
+            raise ValueError("key_lens must be an int32 [B] tensor on the device of q")
+        key_lens = key_lens.contiguous()
+    p = FaProblem(batch=B, heads=H, seqlen=N, head_dim=d,
+                  stride_b=q.stride(0), stride_h=q.stride(1), stride_n=q.stride(2),
+                  scale=float(scale), causal=1 if causal else 0, dtype=_DTYPES[q.dtype],
+                  key_lens=None if key_lens is None else key_lens.data_ptr())
+    return p, key_lens
+
+
+def _same_layout(ref, *others):
+    for t in others:
+        if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype \
+                or t.device != ref.device:
+            raise ValueError("Q, K, V, O and dO must share shape, strides, dtype and device")
+
+
+def _empty_like_layout(q):
+    return torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+
+
+def fa_fwd(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=None):
+    """Exact attention forward; returns (O, LSE).  Calls fa_fwd."""
+    _same_layout(q, k, v)
+    p, kl = _problem(q, scale, causal, key_lens)
+    o = _empty_like_layout(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    _same_layout(q, o)
+    lib = _lib.load()
+    _lib.check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(q)))
+    return o, lse
+
+
+def fa_fwd_blocksparse(q, k, v, block_mask, *, mask_block=128, scale=None, causal=False,
+                       key_lens=None, out=None, lse=None):
+    """Block-sparse forward; ``block_mask`` is uint8 [N/mb, N/mb] (shared by all heads)
+    or [H, N/mb, N/mb].  Returns (O, LSE).  Calls fa_fwd_blocksparse."""
+    _same_layout(q, k, v)
+    p, kl = _problem(q, scale, causal, key_lens)
+    bm, hstride = _mask(block_mask, q)
+    o = _empty_like_layout(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = _lib.load()
+    _lib.check(lib.fa_fwd_blocksparse(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
+                                      _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(q)))
+    return o, lse
+
+
+def _mask(block_mask, q):
+    if block_mask.dtype != torch.uint8 or block_mask.device != q.device:
+        raise ValueError("block_mask must be a uint8 tensor on the device of q")
+    bm = block_mask.contiguous()
+    if bm.dim() == 2:
+        return bm, 0
+    if bm.dim() == 3 and bm.shape[0] == q.shape[1]:
+        return bm, bm.stride(0)
+    raise ValueError("block_mask must be [N/mb, N/mb] or [H, N/mb, N/mb]")
+
+
+def fa_bwd_workspace_bytes(q, *, scale=None, causal=False, key_lens=None) -> int:
+    """Workspace bytes fa_bwd needs for this problem.  Calls fa_bwd_workspace_bytes."""
+    p, _ = _problem(q, scale, causal, key_lens)
+    lib = _lib.load()
+    n = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+    if n == 0:
+        raise FaError(_lib.FA_ERR_INVALID, lib.fa_last_error().decode())
+    return int(n)
+
+
+def _bwd_outputs(q, workspace, p, grads):
+    lib = _lib.load()
+    need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    outs = []
+    for g in grads:
+        if g is None:
+            g = _empty_like_layout(q)
+        else:
+            _same_layout(q, g)
+        outs.append(g)
+    return outs[0], outs[1], outs[2], workspace
+
+
+def fa_bwd(q, k, v, o, lse, do, *, scale=None, causal=False, key_lens=None, workspace=None,
+           dq=None, dk=None, dv=None):
+    """Gradients (dQ, dK, dV) of <dO, O>.  Calls fa_bwd."""
+    _same_layout(q, k, v, o, do)
+    p, kl = _problem(q, scale, causal, key_lens)
+    dq, dk, dv, ws = _bwd_outputs(q, workspace, p, (dq, dk, dv))
+    lib = _lib.load()
+    _lib.check(lib.fa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream(q)))
+    return dq, dk, dv
+
+
+def fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, *, mask_block=128, scale=None,
+                       causal=False, key_lens=None, workspace=None, dq=None, dk=None, dv=None):
+    """Block-sparse gradients (dQ, dK, dV).  Calls fa_bwd_blocksparse."""
+    _same_layout(q, k, v, o, do)
+    p, kl = _problem(q, scale, causal, key_lens)
+    bm, hstride = _mask(block_mask, q)
+    dq, dk, dv, ws = _bwd_outputs(q, workspace, p, (dq, dk, dv))
+    lib = _lib.load()
+    _lib.check(lib.fa_bwd_blocksparse(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
+                                      _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(q)))
+    return dq, dk, dv

@@ -1,0 +1,82 @@
+"""ctypes view of libfa's C ABI (include/fa.h).  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+
+# Every symbol include/fa.h declares.
+EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_bwd_blocksparse", "fa_status_string", "fa_last_error", "fa_abi_version")
+ABI_VERSION = 1
+
+
+class FaProblem(ctypes.Structure):
+    """Mirror of fa_problem_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+        ("stride_n", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("key_lens", ctypes.c_void_p),
+    ]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree).  Raises if it is missing: there is no
+    other implementation to fall back to."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m exact_io_aware_33_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pp = ctypes.POINTER(FaProblem)
+    lib.fa_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_blocksparse.argtypes = [pp, vp, i32, i64, vp, vp, vp, vp, vp, vp]
+    lib.fa_fwd_blocksparse.restype = i32
+    lib.fa_bwd_workspace_bytes.argtypes = [pp]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd_blocksparse.argtypes = [pp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fa_bwd_blocksparse.restype = i32
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i32
+    if lib.fa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libfa ABI version {lib.fa_abi_version()} != {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != FA_OK:
+        lib = load()
+        msg = lib.fa_last_error().decode() or lib.fa_status_string(status).decode()
+        raise FaError(status, f"{lib.fa_status_string(status).decode()}: {msg}")

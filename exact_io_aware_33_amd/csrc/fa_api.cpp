@@ -1,0 +1,211 @@
+// C ABI entry points of libfa (declared in include/fa.h): argument checks on
+// the host, then one launch sequence on the caller's stream.  Every argument
+// error is reported before the first HIP call; nothing here allocates,
+// synchronises or keeps state between calls (apart from the calling thread's
+// last error message).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status_t fail(fa_status_t st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int elem_size(int32_t dt) { return dt == FA_DTYPE_F32 ? 4 : 2; }
+
+// Checks shared by every entry point.
+fa_status_t check_problem(const fa_problem_t *p) {
+  if (!p) return fail(FA_ERR_INVALID, "problem pointer is NULL");
+  if (p->batch <= 0 || p->heads <= 0 || p->seqlen <= 0)
+    return fail(FA_ERR_INVALID, "batch, heads and seqlen must be >= 1 (got %d, %d, %d)", p->batch,
+                p->heads, p->seqlen);
+  if (p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_F16 && p->dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_INVALID, "unknown dtype %d", p->dtype);
+  if (p->head_dim <= 0) return fail(FA_ERR_INVALID, "head_dim must be >= 1 (got %d)", p->head_dim);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", p->head_dim);
+  if (!std::isfinite(p->scale) || p->scale < 0.f)
+    return fail(FA_ERR_INVALID, "scale must be finite and >= 0");
+  const int64_t rows = (int64_t)p->batch * p->heads * p->seqlen;
+  if (rows * p->head_dim >= (int64_t(1) << 31) || rows >= (int64_t(1) << 31))
+    return fail(FA_ERR_UNSUPPORTED, "B*H*N*d exceeds the 32-bit index range");
+  const int es = elem_size(p->dtype);
+  if (p->stride_b < 0 || p->stride_h < 0 || p->stride_n < 0)
+    return fail(FA_ERR_INVALID, "strides must be non-negative");
+  if ((p->stride_b * es) % 16 || (p->stride_h * es) % 16 || (p->stride_n * es) % 16)
+    return fail(FA_ERR_INVALID, "strides must be multiples of 16 bytes");
+  if (p->stride_n < p->head_dim)
+    return fail(FA_ERR_INVALID, "stride_n (%lld) smaller than head_dim", (long long)p->stride_n);
+  if (p->key_lens && !aligned16(p->key_lens))
+    return fail(FA_ERR_INVALID, "key_lens must be 16-byte aligned");
+  return FA_OK;
+}
+
+fa_status_t check_tensor(const void *ptr, const char *name) {
+  if (!ptr) return fail(FA_ERR_INVALID, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(FA_ERR_INVALID, "%s is not 16-byte aligned", name);
+  return FA_OK;
+}
+
+fa_status_t check_mask(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int64_t hstride) {
+  if (!mask) return fail(FA_ERR_INVALID, "block_mask is NULL");
+  if (mb <= 0) return fail(FA_ERR_INVALID, "mask_block must be >= 1 (got %d)", mb);
+  if (p->seqlen % mb) return fail(FA_ERR_INVALID, "mask_block %d does not divide N = %d", mb, p->seqlen);
+  if (mb % 128) return fail(FA_ERR_UNSUPPORTED, "mask_block %d is not a multiple of 128", mb);
+  if (p->seqlen / mb > 1024) return fail(FA_ERR_UNSUPPORTED, "N / mask_block exceeds 1024");
+  if (hstride < 0) return fail(FA_ERR_INVALID, "mask_head_stride must be >= 0");
+  return FA_OK;
+}
+
+fa::AttnParams make_params(const fa_problem_t *p) {
+  fa::AttnParams a{};
+  a.B = p->batch;
+  a.H = p->heads;
+  a.N = p->seqlen;
+  a.d = p->head_dim;
+  a.sb = p->stride_b;
+  a.sh = p->stride_h;
+  a.sn = p->stride_n;
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * fa::kLog2eHost;
+  a.causal = p->causal != 0;
+  a.key_lens = p->key_lens;
+  return a;
+}
+
+fa_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  return fail(FA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+}
+
+fa_status_t fwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int64_t hstride,
+                     bool sparse, const void *q, const void *k, const void *v, void *o, float *lse,
+                     void *stream) {
+  g_err[0] = 0;
+  fa_status_t st;
+  if ((st = check_problem(p)) != FA_OK) return st;
+  if ((st = check_tensor(q, "q")) != FA_OK || (st = check_tensor(k, "k")) != FA_OK ||
+      (st = check_tensor(v, "v")) != FA_OK || (st = check_tensor(o, "o")) != FA_OK ||
+      (st = check_tensor(lse, "lse")) != FA_OK)
+    return st;
+  if (sparse && (st = check_mask(p, mask, mb, hstride)) != FA_OK) return st;
+  fa::AttnParams a = make_params(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  if (sparse) {
+    a.mask = mask;
+    a.mb = mb;
+    a.nblk = p->seqlen / mb;
+    a.mask_hstride = hstride;
+  }
+  return hip_status(fa::launch_fwd(a, (fa_dtype_t)p->dtype, sparse, (hipStream_t)stream));
+}
+
+fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int64_t hstride,
+                     bool sparse, const void *q, const void *k, const void *v, const void *o,
+                     const float *lse, const void *dout, void *dq, void *dk, void *dv, void *ws,
+                     size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  fa_status_t st;
+  if ((st = check_problem(p)) != FA_OK) return st;
+  if ((st = check_tensor(q, "q")) != FA_OK || (st = check_tensor(k, "k")) != FA_OK ||
+      (st = check_tensor(v, "v")) != FA_OK || (st = check_tensor(o, "o")) != FA_OK ||
+      (st = check_tensor(lse, "lse")) != FA_OK || (st = check_tensor(dout, "dout")) != FA_OK ||
+      (st = check_tensor(dq, "dq")) != FA_OK || (st = check_tensor(dk, "dk")) != FA_OK ||
+      (st = check_tensor(dv, "dv")) != FA_OK || (st = check_tensor(ws, "workspace")) != FA_OK)
+    return st;
+  if (sparse && (st = check_mask(p, mask, mb, hstride)) != FA_OK) return st;
+  const int64_t rows = (int64_t)p->batch * p->heads * p->seqlen;
+  const size_t need = fa::ws_total_bytes(rows, p->head_dim);
+  if (ws_bytes < need)
+    return fail(FA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
+  fa::AttnParams a = make_params(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o_in = o;
+  a.lse = const_cast<float *>(lse);
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws_delta = static_cast<float *>(ws);
+  a.ws_dq = reinterpret_cast<float *>(static_cast<char *>(ws) + fa::ws_delta_bytes(rows));
+  if (sparse) {
+    a.mask = mask;
+    a.mb = mb;
+    a.nblk = p->seqlen / mb;
+    a.mask_hstride = hstride;
+  }
+  return hip_status(fa::launch_bwd(a, (fa_dtype_t)p->dtype, sparse, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd(const fa_problem_t *p, const void *q, const void *k, const void *v, void *o,
+                   float *lse, void *stream) {
+  return fwd_impl(p, nullptr, 0, 0, false, q, k, v, o, lse, stream);
+}
+
+fa_status_t fa_fwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask, int32_t mask_block,
+                               int64_t mask_head_stride, const void *q, const void *k, const void *v,
+                               void *o, float *lse, void *stream) {
+  return fwd_impl(p, block_mask, mask_block, mask_head_stride, true, q, k, v, o, lse, stream);
+}
+
+size_t fa_bwd_workspace_bytes(const fa_problem_t *p) {
+  g_err[0] = 0;
+  if (check_problem(p) != FA_OK) return 0;
+  const int64_t rows = (int64_t)p->batch * p->heads * p->seqlen;
+  return fa::ws_total_bytes(rows, p->head_dim);
+}
+
+fa_status_t fa_bwd(const fa_problem_t *p, const void *q, const void *k, const void *v, const void *o,
+                   const float *lse, const void *dout, void *dq, void *dk, void *dv, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  return bwd_impl(p, nullptr, 0, 0, false, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                  workspace_bytes, stream);
+}
+
+fa_status_t fa_bwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask, int32_t mask_block,
+                               int64_t mask_head_stride, const void *q, const void *k, const void *v,
+                               const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                               void *dv, void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl(p, block_mask, mask_block, mask_head_stride, true, q, k, v, o, lse, dout, dq, dk, dv,
+                  workspace, workspace_bytes, stream);
+}
+
+const char *fa_status_string(fa_status_t status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID: return "FA_ERR_INVALID: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: configuration not built";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown fa_status_t";
+}
+
+const char *fa_last_error(void) { return g_err; }
+
+int32_t fa_abi_version(void) { return FA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// MFMA wrappers per storage type, LDS fragment reads, cross-half-wave
+// exchange, and the workgroup -> tile mapping.
+//
+// Matrix-core conventions used throughout (CDNA3/CDNA4 MFMA lane layouts,
+// checked on gfx950 by an in-bounds probe):
+//   32x32 MFMA with K = 2*KPL: lane l holds A[m = l%32][k = KPL*(l/32) + e] and
+//     B[k = KPL*(l/32) + e][n = l%32], e < KPL; the 16 accumulator registers
+//     hold C[8*(r/4) + 4*(l/32) + r%4][l%32], r < 16.
+//   16x16 MFMA with K = 4*KPL: lane l holds A[m = l%16][k = KPL*(l/16) + e],
+//     B[k = KPL*(l/16) + e][n = l%16]; accumulators C[4*(l/16) + r][l%16].
+// KPL = 8 for 16-bit types (v_mfma_f32_32x32x16_{f16,bf16},
+// v_mfma_f32_16x16x32_{f16,bf16}) and KPL = 1 for fp32 (32x32x2, 16x16x4).
+//
+// "Register order": the 32x32 accumulator register r of a lane in half h
+// holds row 8*(r/4) + 4*h + r%4.  A product that contracts over those rows can
+// feed the accumulator registers (converted) straight back as an MFMA operand,
+// as long as its other operand enumerates the contraction index in the same
+// order: step t, element e <-> register KPL*t + e.  reg_row() gives that row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Row held by accumulator register r of a lane in half-wave h (32x32 layout).
+__device__ __forceinline__ constexpr int reg_row(int r, int h) {
+  return 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
+template <typename T> struct Mma;
+
+template <> struct Mma<__bf16> {
+  static constexpr int KPL = 8;
+  using frag = bf16x8;
+  __device__ static __forceinline__ f32x16 mma32(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mma16(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<_Float16> {
+  static constexpr int KPL = 8;
+  using frag = f16x8;
+  __device__ static __forceinline__ f32x16 mma32(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mma16(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KPL = 1;
+  using frag = float;
+  __device__ static __forceinline__ f32x16 mma32(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mma16(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// ---- conversions -----------------------------------------------------------
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+
+// Pack KPL consecutive fp32 registers (starting at element `first` of a
+// 16-register accumulator) into an MFMA operand of type T.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag pack_frag(const f32x16 &acc, int first) {
+  if constexpr (Mma<T>::KPL == 1) {
+    return acc[first];
+  } else {
+    typename Mma<T>::frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (T)acc[first + e];
+    return f;
+  }
+}
+
+// ---- global memory -----------------------------------------------------------
+__device__ __forceinline__ u32x4 ldg16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void stg16(void *p, u32x4 v) {
+  *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// ---- LDS reads ---------------------------------------------------------------
+// KPL contiguous elements of type T at byte offset `off` of LDS.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag lds_frag(const char *lds, int off) {
+  return *reinterpret_cast<const typename Mma<T>::frag *>(lds + off);
+}
+
+// Transposed fragment read for 16-bit types (ds_read_b64_tr_b16).  Within each
+// group of 16 lanes the instruction returns to lane i, element e, the element
+// (i % 4) of the 8 bytes read by source lane 4*e + i/4.  So if every lane of a
+// group addresses  base + row(s/4) * pitch + (col0 + 4*(s%4)) * 2,  s = lane%16,
+// lane i receives M[row(e)][col0 + i] for e = 0..3: four rows of one column.
+__device__ __forceinline__ i16x4 lds_tr4(const char *lds, int byte_off) {
+  // `lds` points into a __shared__ array: the cast is an address-space cast
+  // from the generic to the LDS address space.
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)(lds + byte_off));
+}
+
+// Cross half-wave exchange: value held by lane l ^ 32.
+__device__ __forceinline__ float xor32(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // lanes < 32 get (own, partner) ; lanes >= 32 get (partner, own)
+  return (threadIdx.x & 32) ? __uint_as_float(s[0]) : __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- workgroup -> tile mapping ----------------------------------------------
+// Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that each
+// XCD receives a contiguous range of logical ids (consecutive tiles of the same
+// (batch, head), which then share K/V in that XCD's L2).  Bijective for any
+// grid size; correctness does not depend on the dispatch order.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  constexpr int kXcd = 8;
+  const int per = total / kXcd, rem = total % kXcd;
+  const int xcd = id % kXcd, slot = id / kXcd;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+}
+
+}  // namespace fa

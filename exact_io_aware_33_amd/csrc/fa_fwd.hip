@@ -1,0 +1,333 @@
+// Forward pass of exact attention on gfx950: one workgroup per (batch, head,
+// 128-query tile), one wavefront per 32 queries, K/V streamed through LDS in
+// tiles of BC keys with a running row max / row sum.
+//
+// Method (FlashAttention summary page, paper 2205.14135):
+//  * section "Incremental softmax tracking", steps 1-4 for query block i and
+//    key/value block j: block scores, block max / exp / sum, running max/sum
+//    update, rescaled output accumulation.  Here the division by the running
+//    sum is deferred to the epilogue (identical in exact arithmetic) and the
+//    exponentials are taken directly against the running max (the block-local
+//    exp(S - m_block) times exp(m_block - m_new) of the page, folded).
+//  * section "Key ideas", tiling bullet: Q, K, V are cut into blocks that fit
+//    on chip; the N x N matrices never reach device memory.
+//  * Math-properties page, section 7: the loop keeps one query tile resident
+//    (outer loop) and streams key/value tiles (inner loop); the carried state
+//    is the running max, the exponential sum and the partial output.
+//  * section "Block-Sparse FlashAttention": only key tiles whose mask block is
+//    set are visited.
+//
+// gfx950 mapping.  Scores are formed transposed, S^T = K Q^T, on 32x32 MFMAs
+// (A = K rows from LDS, B = this wave's Q rows kept in registers for the whole
+// loop), so every lane owns one query (column) and 16 of its keys per 32-key
+// block; its partner lane (l ^ 32) owns the other 16.  The row max therefore
+// needs one cross-half exchange, and P^T, converted in registers, is directly
+// the B operand of O^T += V^T P^T.  V^T fragments come from the row-major V
+// tile in LDS through the transposing LDS read (ds_read_b64_tr_b16).
+// Exponentials are base 2 with scale*log2(e) folded into one FMA.
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+
+template <typename T, int D>
+struct FwdCfg {
+  static constexpr int E = sizeof(T);
+  static constexpr int KPL = Mma<T>::KPL;
+  static constexpr int WAVES = 4;
+  static constexpr int BR = 32 * WAVES;           // queries per workgroup
+  static constexpr int BC = (E == 4) ? 32 : 64;   // keys per LDS tile
+  static constexpr int NSB = BC / 32;             // 32-key score blocks per tile
+  static constexpr int NOB = D / 32;              // 32-wide blocks of the output
+  static constexpr int KSTEPS = D / (2 * KPL);    // MFMA steps over d
+  static constexpr int PSTEPS = 16 / KPL;         // MFMA steps over 32 keys
+  static constexpr int PITCH = D * E + 16;        // LDS row pitch (bytes)
+  static constexpr int TILE_BYTES = BC * PITCH;
+  static constexpr int CPR = D * E / 16;          // 16-byte chunks per row
+  static constexpr int CPT = BC * CPR / (64 * WAVES);  // chunks per thread
+  static_assert(BC * CPR % (64 * WAVES) == 0, "tile must split evenly");
+};
+
+constexpr int kMaxMaskBlocks = 1024;
+
+// V^T fragment for step t of 32-key block sb and 32-wide output block nb:
+// element e is V[sb*32 + reg_row(KPL*t + e, h)][nb*32 + l32].
+template <typename T, int PITCH>
+__device__ __forceinline__ typename Mma<T>::frag vt_frag(const char *vl, int sb, int t, int nb) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (Mma<T>::KPL == 1) {
+    const int row = sb * 32 + reg_row(t, lane >> 5);
+    return *reinterpret_cast<const float *>(vl + row * PITCH + (nb * 32 + (lane & 31)) * 4);
+  } else {
+    const int g = lane >> 4, s16 = lane & 15;
+    const int row0 = sb * 32 + 16 * t + 4 * (g >> 1) + (s16 >> 2);
+    const int col = nb * 32 + 16 * (g & 1) + 4 * (s16 & 3);
+    const i16x4 lo = lds_tr4(vl, row0 * PITCH + col * 2);
+    const i16x4 hi = lds_tr4(vl, (row0 + 8) * PITCH + col * 2);
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(typename Mma<T>::frag, v);
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+__global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
+  using C = FwdCfg<T, D>;
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int KPL = C::KPL, PITCH = C::PITCH, E = C::E;
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * C::TILE_BYTES];
+  __shared__ uint16_t blist[SPARSE ? kMaxMaskBlocks : 1];
+  __shared__ int nlist_s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int N = p.N;
+  const int nqt = (N + C::BR - 1) / C::BR;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / nqt;
+  int qt = logical - bh * nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
+  const int b = bh / p.H, hh = bh - b * p.H;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;
+  const T *Q = static_cast<const T *>(p.q) + base;
+  const T *K = static_cast<const T *>(p.k) + base;
+  const T *V = static_cast<const T *>(p.v) + base;
+  T *O = static_cast<T *>(p.o) + base;
+
+  int kv_len = N;
+  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
+  const int q_tile0 = qt * C::BR;
+  const int qw0 = q_tile0 + 32 * wave;  // first query of this wave
+  const int qi = qw0 + l32;             // this lane's query
+  int kv_hi = kv_len;                   // keys >= kv_hi are invisible to the whole tile
+  if (CAUSAL) kv_hi = min(kv_hi, q_tile0 + C::BR);
+
+  // ---- the list of key tiles this workgroup visits
+  int ntiles;
+  int tiles_per_blk = 1;
+  if constexpr (SPARSE) {
+    tiles_per_blk = p.mb / C::BC;
+    const uint8_t *mrow = p.mask + (int64_t)hh * p.mask_hstride + (int64_t)(q_tile0 / p.mb) * p.nblk;
+    if (wave == 0) {
+      int count = 0;
+      for (int j0 = 0; j0 < p.nblk; j0 += 64) {
+        const int j = j0 + lane;
+        const bool set = j < p.nblk && j * p.mb < kv_hi && mrow[j] != 0;
+        const uint64_t bal = __ballot(set);
+        if (set) blist[count + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)j;
+        count += __popcll(bal);
+      }
+      if (lane == 0) nlist_s = count;
+    }
+    __syncthreads();
+    const int nl = nlist_s;
+    if (nl == 0) {
+      ntiles = 0;
+    } else {
+      const int last0 = (int)blist[nl - 1] * p.mb;
+      const int in_last = min(tiles_per_blk, (kv_hi - last0 + C::BC - 1) / C::BC);
+      ntiles = (nl - 1) * tiles_per_blk + in_last;
+    }
+  } else {
+    ntiles = (kv_hi + C::BC - 1) / C::BC;
+  }
+  auto tile_start = [&](int t) -> int {
+    if constexpr (SPARSE) {
+      const int bi = t / tiles_per_blk;
+      return (int)blist[bi] * p.mb + (t - bi * tiles_per_blk) * C::BC;
+    } else {
+      return t * C::BC;
+    }
+  };
+
+  // ---- this wave's Q rows, held as MFMA B operands for the whole loop.
+  // Step s, half h covers d = h*D/2 + s*KPL + e: each lane reads a contiguous
+  // half row.
+  frag qf[C::KSTEPS];
+  if (qi < N) {
+    const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
+  } else {
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = frag{};
+  }
+
+  // ---- K/V staging: global -> registers (next tile) -> LDS (double buffer)
+  u32x4 stk[C::CPT], stv[C::CPT];
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+      const int key = kv0 + row;
+      if (key < N) {
+        stk[u] = ldg16(reinterpret_cast<const char *>(K + (int64_t)key * p.sn) + col * 16);
+        stv[u] = ldg16(reinterpret_cast<const char *>(V + (int64_t)key * p.sn) + col * 16);
+      } else {
+        stk[u] = u32x4{0, 0, 0, 0};
+        stv[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char *kl = smem + buf * 2 * C::TILE_BYTES;
+    char *vl = kl + C::TILE_BYTES;
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+      *reinterpret_cast<u32x4 *>(kl + row * PITCH + col * 16) = stk[u];
+      *reinterpret_cast<u32x4 *>(vl + row * PITCH + col * 16) = stv[u];
+    }
+  };
+
+  float m_run = -INFINITY;  // running max of scale*log2(e)*S, this lane's query
+  float l_run = 0.f;        // running sum over this lane's half of the keys
+  f32x16 oacc[C::NOB];
+#pragma unroll
+  for (int nb = 0; nb < C::NOB; ++nb) oacc[nb] = f32x16{};
+  const float c2 = p.scale_log2;
+
+  if (ntiles > 0) {
+    load_tile(tile_start(0));
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int kv0 = tile_start(it);
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(tile_start(it + 1));
+    const char *kl = smem + (it & 1) * 2 * C::TILE_BYTES;
+    const char *vl = kl + C::TILE_BYTES;
+
+    const bool skip = CAUSAL && kv0 > qw0 + 31;  // tile invisible to this wave
+    if (!skip) {
+      // step 1: S^T = K_j Q_i^T
+      f32x16 sacc[C::NSB];
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        sacc[sb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+          const frag a = lds_frag<T>(kl, (sb * 32 + l32) * PITCH + (h * (D / 2) + s * KPL) * E);
+          sacc[sb] = M::mma32(a, qf[s], sacc[sb]);
+        }
+      }
+      // masking of boundary tiles (padding / ragged end / causal diagonal)
+      const bool need_mask = (kv0 + C::BC > kv_len) || (CAUSAL && kv0 + C::BC - 1 > qw0);
+      float mx = -INFINITY;
+      if (need_mask) {
+#pragma unroll
+        for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + sb * 32 + reg_row(r, h);
+            const bool ok = key < kv_len && (!CAUSAL || key <= qi);
+            if (!ok) sacc[sb][r] = -INFINITY;
+            mx = fmaxf(mx, sacc[sb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
+      }
+      // steps 2-3: running max and rescale of the carried state
+      mx = fmaxf(mx, xor32(mx));
+      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < C::NOB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+      float lsum = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = fast_exp2(fmaf(sacc[sb][r], c2, -m_use));
+          if (need_mask && sacc[sb][r] == -INFINITY) x = 0.f;
+          sacc[sb][r] = x;
+          lsum += x;
+        }
+      l_run += lsum;
+      // step 4: O_i^T += V_j^T P^T
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+        for (int t = 0; t < C::PSTEPS; ++t) {
+          const frag pb = pack_frag<T>(sacc[sb], t * KPL);
+#pragma unroll
+          for (int nb = 0; nb < C::NOB; ++nb)
+            oacc[nb] = M::mma32(vt_frag<T, PITCH>(vl, sb, t, nb), pb, oacc[nb]);
+        }
+    }
+    if (has_next) store_tile((it + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qi < N) {
+    T *orow = O + (int64_t)qi * p.sn;
+#pragma unroll
+    for (int nb = 0; nb < C::NOB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = nb * 32 + 8 * i + 4 * h;
+        if constexpr (E == 4) {
+          f32x4 v = {oacc[nb][4 * i] * inv, oacc[nb][4 * i + 1] * inv, oacc[nb][4 * i + 2] * inv,
+                     oacc[nb][4 * i + 3] * inv};
+          *reinterpret_cast<f32x4 *>(orow + d0) = v;
+        } else {
+          typedef T t4 __attribute__((ext_vector_type(4)));
+          t4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = (T)(oacc[nb][4 * i + j] * inv);
+          *reinterpret_cast<t4 *>(orow + d0) = v;
+        }
+      }
+    if (h == 0)
+      p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+static hipError_t launch_fwd_t(const AttnParams &p, hipStream_t s) {
+  using C = FwdCfg<T, D>;
+  const int64_t nqt = (p.N + C::BR - 1) / C::BR;
+  const int64_t grid = (int64_t)p.B * p.H * nqt;
+  AttnParams a = p;
+  void *args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE>),
+                         dim3((unsigned)grid), dim3(256), args, 0, s);
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_d(const AttnParams &p, bool sparse, hipStream_t s) {
+  if (sparse) return p.causal ? launch_fwd_t<T, D, true, true>(p, s) : launch_fwd_t<T, D, false, true>(p, s);
+  return p.causal ? launch_fwd_t<T, D, true, false>(p, s) : launch_fwd_t<T, D, false, false>(p, s);
+}
+
+template <typename T>
+static hipError_t launch_fwd_dt(const AttnParams &p, bool sparse, hipStream_t s) {
+  return p.d == 64 ? launch_fwd_d<T, 64>(p, sparse, s) : launch_fwd_d<T, 128>(p, sparse, s);
+}
+
+hipError_t launch_fwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s) {
+  switch (dt) {
+    case FA_DTYPE_F32: return launch_fwd_dt<float>(p, sparse, s);
+    case FA_DTYPE_F16: return launch_fwd_dt<_Float16>(p, sparse, s);
+    case FA_DTYPE_BF16: return launch_fwd_dt<__bf16>(p, sparse, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,50 @@
+// Host/device parameter blocks and the launcher interface between the C ABI
+// (fa_api.cpp) and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Everything a kernel needs, by value (one kernel argument).
+struct AttnParams {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  // backward only
+  const void *o_in;   // forward output, read by the preprocess kernel
+  const void *dout;
+  void *dq, *dk, *dv;
+  float *ws_delta;    // [B*H*N]  rowsum(dO * O)
+  float *ws_dq;       // [B*H*N*d] float32 dQ accumulator (contiguous)
+  // problem
+  int32_t B, H, N, d;
+  int64_t sb, sh, sn;        // element strides of the [B,H,N,d] tensors
+  float scale;               // softmax scale
+  float scale_log2;          // scale * log2(e)
+  int32_t causal;
+  const int32_t *key_lens;   // device [B] or nullptr
+  // block sparsity
+  const uint8_t *mask;       // device [N/mb, N/mb] (+ head stride) or nullptr
+  int32_t mb;                // block size (multiple of 128)
+  int32_t nblk;              // N / mb
+  int64_t mask_hstride;      // bytes between heads' masks (0 = shared)
+};
+
+// Launchers (defined in fa_fwd.hip / fa_bwd.hip).  They assume validated
+// arguments and return hipSuccess or the launch error.
+hipError_t launch_fwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s);
+hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s);
+
+// Workspace layout shared by fa_api.cpp and fa_bwd.hip.
+inline size_t ws_delta_bytes(int64_t rows) { return (size_t)((rows * 4 + 255) / 256 * 256); }
+inline size_t ws_total_bytes(int64_t rows, int64_t d) {
+  return ws_delta_bytes(rows) + (size_t)(rows * d * 4);
+}
+
+}  // namespace fa

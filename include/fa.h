@@ -1,0 +1,173 @@
+/*
+ * fa.h -- C ABI of libfa: exact, tiled scaled-dot-product attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (FlashAttention summary page, paper 2205.14135, section
+ * "Problem and motivation"): for every batch b and head h,
+ *     S = scale * Q K^T,   P = softmax(S) row by row,   O = P V,
+ * with Q, K, V, O in R^{N x d}.  The score matrix S and the probabilities P
+ * never reach device memory: they live in registers one tile at a time
+ * (same page, "Key ideas": tiling and recomputation; section "Incremental
+ * softmax tracking": the running max / running sum update).
+ *
+ * Masking (same page, "Key ideas", kernel-fusion bullet names masking; section
+ * "Block-Sparse FlashAttention" defines the block mask).  Key j is visible to
+ * query i iff every active rule allows it:
+ *   causal      : j <= i                       (fa_problem_t.causal != 0)
+ *   key padding : j < key_lens[b]              (fa_problem_t.key_lens != NULL;
+ *                                               values are clamped to [0, N])
+ *   block mask  : M[i / mb][j / mb] != 0        (the *_blocksparse entry points)
+ * A query row with no visible key gets O = 0, LSE = -inf and zero gradients.
+ *
+ * Saved statistics: the forward pass writes LSE_i = m_i + ln(l_i), the natural
+ * log-sum-exp of the scaled, masked score row i (the summary page keeps (l, m)
+ * for the backward pass; LSE carries the same information, P = exp(S - LSE)).
+ *
+ * Backward: the gradients of <dO, O> with respect to Q, K and V, computed by
+ * recomputing S and P tile by tile from Q, K, V, O and LSE (summary page,
+ * "Key ideas", recomputation bullet).  The gradient formulas themselves are
+ * the analytic derivatives of the definition above.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d] arrays of the problem's
+ *   dtype, with element strides (stride_b, stride_h, stride_n) shared by all of
+ *   them and a unit stride along d.  LSE is a contiguous float32 [B, H, N].
+ *   A contiguous [B, H, N, d] array has strides (H*N*d, N*d, d); a [B, N, H, d]
+ *   array has (N*H*d, d, H*d).
+ * Memory.  Every data pointer is a DEVICE pointer owned by the caller; the
+ *   library never allocates, frees or keeps device memory between calls and
+ *   holds no state, so concurrent calls on different streams are safe.
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ *   enqueue work and return; the caller synchronises before reading results
+ *   and keeps every buffer alive until then.
+ * Alignment.  Q, K, V, O, dO, dQ, dK, dV must be 16-byte aligned and the three
+ *   strides multiples of 16 bytes; LSE, key_lens and the workspace 16-byte
+ *   aligned.
+ * Errors.  Argument errors are detected on the host before any HIP call and
+ *   returned synchronously (FA_ERR_INVALID, FA_ERR_UNSUPPORTED); a failed
+ *   launch returns FA_ERR_HIP.  Faults during execution surface at the
+ *   caller's next synchronisation, as usual for HIP.  Nothing aborts or throws
+ *   across this boundary.  fa_last_error() gives a message for the last failed
+ *   call on the calling thread.
+ * Supported shapes.  dtype FP16 or BF16 with d in {64, 128}; dtype FP32 with
+ *   d in {64, 128}.  N >= 1 (any value, not only multiples of the tile),
+ *   B >= 1, H >= 1, B*H*N < 2^31.  scale finite and >= 0.
+ */
+#ifndef EXACT_IO_AWARE_FA_H
+#define EXACT_IO_AWARE_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum fa_dtype {
+  FA_DTYPE_F32 = 0,   /* IEEE float32 storage, float32 arithmetic            */
+  FA_DTYPE_F16 = 1,   /* IEEE float16 storage, float32 accumulation          */
+  FA_DTYPE_BF16 = 2   /* bfloat16 storage, float32 accumulation              */
+} fa_dtype_t;
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID = 1,      /* bad argument: NULL pointer, size <= 0, non-finite
+                              or negative scale, workspace too small, block size
+                              that does not divide N, misaligned pointer       */
+  FA_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim / dtype pair,
+                              block size not a multiple of 128, sizes over the
+                              32-bit index range                              */
+  FA_ERR_HIP = 3           /* the HIP runtime refused a launch                 */
+} fa_status_t;
+
+/* One attention problem.  Shared by the forward and backward entry points. */
+typedef struct fa_problem {
+  int32_t batch;            /* B >= 1                                          */
+  int32_t heads;            /* H >= 1                                          */
+  int32_t seqlen;           /* N >= 1: number of queries = number of keys      */
+  int32_t head_dim;         /* d: 64 or 128                                    */
+  int64_t stride_b;         /* element stride between batches                  */
+  int64_t stride_h;         /* element stride between heads                    */
+  int64_t stride_n;         /* element stride between rows (tokens)            */
+  float scale;              /* S = scale * Q K^T; finite, >= 0 (1/sqrt(d) usual) */
+  int32_t causal;           /* nonzero: key j visible to query i only if j <= i */
+  int32_t dtype;            /* fa_dtype_t                                      */
+  const int32_t *key_lens;  /* device int32 [B] or NULL (no padding): keys
+                               j >= key_lens[b] are masked for every query and
+                               head of batch b; clamped to [0, N] on device    */
+} fa_problem_t;
+
+/* Forward pass (summary page, "Incremental softmax tracking", steps 1-4).
+ *   q, k, v : device [B,H,N,d] inputs (dtype), read only.
+ *   o       : device [B,H,N,d] output (dtype), written in full (rows of fully
+ *             masked queries are written as zeros).
+ *   lse     : device float32 [B,H,N] output, contiguous, written in full.
+ * Returns FA_OK once the work is enqueued on `stream`. */
+fa_status_t fa_fwd(const fa_problem_t *p, const void *q, const void *k,
+                   const void *v, void *o, float *lse, void *stream);
+
+/* Block-sparse forward (summary page, section "Block-Sparse FlashAttention":
+ * only the nonzero blocks of M in {0,1}^{N/mb x N/mb} are evaluated).
+ *   block_mask       : device uint8 [N/mb, N/mb], row-major (row = query
+ *                      block, column = key block); nonzero = evaluate.
+ *   mask_block       : mb, a positive multiple of 128 that divides N.
+ *   mask_head_stride : bytes between the masks of consecutive heads, or 0 for
+ *                      one mask shared by all heads (the mask of head h is at
+ *                      block_mask + h * mask_head_stride; one per head, shared
+ *                      by all batches).
+ * The other arguments and the causal / key_lens fields act as in fa_fwd; all
+ * active masks are combined with AND.  N / mb must not exceed 1024. */
+fa_status_t fa_fwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
+                               int32_t mask_block, int64_t mask_head_stride,
+                               const void *q, const void *k, const void *v,
+                               void *o, float *lse, void *stream);
+
+/* Size in bytes of the device workspace fa_bwd needs for problem p (0 if p is
+ * invalid).  It holds one float32 per query row (rowsum(dO * O)) and a float32
+ * [B,H,N,d] accumulator for dQ: O(N d) extra memory, never O(N^2). */
+size_t fa_bwd_workspace_bytes(const fa_problem_t *p);
+
+/* Backward pass: gradients of <dO, O> (summary page, "Key ideas",
+ * recomputation bullet: S and P are rebuilt per tile from Q, K, V, O, LSE).
+ *   q, k, v, o : the forward's inputs and output (dtype), read only.
+ *   lse        : the forward's float32 [B,H,N] statistics, read only.
+ *   dout       : device [B,H,N,d] upstream gradient dO (dtype), read only.
+ *   dq, dk, dv : device [B,H,N,d] outputs (dtype), written in full.
+ *   workspace  : device scratch of at least fa_bwd_workspace_bytes(p) bytes,
+ *                owned by the caller, contents on entry ignored; it must not
+ *                be shared with a concurrently running call.
+ * The mask fields of p must equal those used for the forward pass. */
+fa_status_t fa_bwd(const fa_problem_t *p, const void *q, const void *k,
+                   const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Block-sparse backward: fa_bwd restricted to the nonzero blocks of the mask,
+ * whose arguments mean what they mean for fa_fwd_blocksparse.  Keys that no
+ * query sees get dK = dV = 0. */
+fa_status_t fa_bwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
+                               int32_t mask_block, int64_t mask_head_stride,
+                               const void *q, const void *k, const void *v,
+                               const void *o, const float *lse,
+                               const void *dout, void *dq, void *dk, void *dv,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *fa_status_string(fa_status_t status);
+
+/* Message describing the last failed call made by the calling thread ("" if
+ * none).  The pointer stays valid until that thread's next library call. */
+const char *fa_last_error(void);
+
+/* FA_ABI_VERSION of the loaded library. */
+int32_t fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_IO_AWARE_FA_H */

@@ -13,8 +13,8 @@ from them.
   method's own algorithm.
 """
 from .attention import (allowed_mask, forward, backward, forward_rows,
-                        probabilities)
+                        gradients_sampled, probabilities)
 from .streaming import merge_stats, streaming_forward
 
 __all__ = ["allowed_mask", "forward", "backward", "forward_rows",
-           "probabilities", "merge_stats", "streaming_forward"]
+           "probabilities", "gradients_sampled", "merge_stats", "streaming_forward"]

@@ -33,7 +33,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["allowed_mask", "forward", "forward_rows", "backward", "probabilities"]
+__all__ = ["allowed_mask", "forward", "forward_rows", "backward", "probabilities",
+           "gradients_sampled"]
 
 
 def _block_mask_for_head(block_mask, h):
@@ -191,3 +192,59 @@ def backward(q, k, v, do, scale, *, causal=False, key_lens=None, block_mask=None
     if return_aux:
         return dq, dk, dv, (o, lse, D_p, D_o)
     return dq, dk, dv
+
+
+def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=None,
+                      block_mask=None, mb=128, chunk=1024):
+    """Exact gradients of one (batch, head) at selected rows / columns only.
+
+    Same definition as :func:`backward`; used at sizes where the full N x d
+    gradients take too long in fp64.  Returns (o_rows [R,d], lse_rows [R],
+    dq_rows [R,d], dk_cols [C,d], dv_cols [C,d]).
+
+    dQ_i needs only row i of P and dP.  dK_j and dV_j need column j of P and
+    dS for every query row i, hence every row's LSE and D_i = rowsum(P * dP):
+    a first pass over all rows (in chunks) computes them, a second forms the
+    selected columns.
+    """
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    N = k.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    lse_all = np.empty(N)
+    D_all = np.empty(N)
+    for r0 in range(0, N, chunk):
+        rr = np.arange(r0, min(N, r0 + chunk))
+        s = float(scale) * (q[rr] @ k.T)
+        a = allowed_mask(rr, N, causal=causal, key_len=key_len, block_mask=block_mask, mb=mb)
+        s = np.where(a, s, -np.inf)
+        m, l, valid, e = _row_softmax_stats(s)
+        p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
+        dp = do[rr] @ v.T
+        lse_all[rr] = np.where(valid, m + np.log(np.where(valid, l, 1.0)), -np.inf)
+        D_all[rr] = np.sum(p * dp, axis=1)
+    # selected rows: O, LSE, dQ
+    s = float(scale) * (q[rows] @ k.T)
+    a = allowed_mask(rows, N, causal=causal, key_len=key_len, block_mask=block_mask, mb=mb)
+    s = np.where(a, s, -np.inf)
+    lr = lse_all[rows]
+    fin = np.isfinite(lr)
+    p = np.where(fin[:, None], np.exp(s - np.where(fin, lr, 0.0)[:, None]), 0.0)
+    o_rows = p @ v
+    ds = p * ((do[rows] @ v.T) - D_all[rows][:, None])
+    dq_rows = float(scale) * (ds @ k)
+    # selected columns: dK, dV
+    dk_cols = np.zeros((cols.size, q.shape[1]))
+    dv_cols = np.zeros((cols.size, v.shape[1]))
+    for r0 in range(0, N, chunk):
+        rr = np.arange(r0, min(N, r0 + chunk))
+        s = float(scale) * (q[rr] @ k[cols].T)
+        a = allowed_mask(rr, N, causal=causal, key_len=key_len, block_mask=block_mask, mb=mb)[:, cols]
+        s = np.where(a, s, -np.inf)
+        lc = lse_all[rr]
+        fin = np.isfinite(lc)
+        p = np.where(fin[:, None], np.exp(s - np.where(fin, lc, 0.0)[:, None]), 0.0)
+        ds = p * ((do[rr] @ v[cols].T) - D_all[rr][:, None])
+        dk_cols += float(scale) * (ds.T @ q[rr])
+        dv_cols += p.T @ do[rr]
+    return o_rows, lse_all[rows], dq_rows, dk_cols, dv_cols

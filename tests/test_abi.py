@@ -1,0 +1,148 @@
+"""The C ABI on the CPU: the library loads, exports what include/fa.h
+declares, and rejects bad arguments synchronously, before any HIP call (so no
+GPU is needed).  No compute call is made here."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from exact_io_aware_33_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+INVALID, UNSUPPORTED = _lib.FA_ERR_INVALID, _lib.FA_ERR_UNSUPPORTED
+A = 0x10000          # fake, 16-byte aligned "device" address (never dereferenced)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(fa_[a-z_]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def prob(**kw):
+    p = dict(batch=2, heads=3, seqlen=256, head_dim=64, stride_b=3 * 256 * 64, stride_h=256 * 64,
+             stride_n=64, scale=0.125, causal=0, dtype=_lib.FA_DTYPE_BF16, key_lens=None)
+    p.update(kw)
+    return _lib.FaProblem(**p)
+
+
+def fwd(lib, p, q=A, k=A, v=A, o=A, lse=A):
+    return lib.fa_fwd(ctypes.byref(p), q, k, v, o, lse, None)
+
+
+def bwd(lib, p, ws_bytes=None, **ptrs):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, ws=A)
+    a.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+    return lib.fa_bwd(ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                      a["dk"], a["dv"], a["ws"], ws_bytes, None)
+
+
+def test_exports_match_header(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.fa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in range(4):
+        assert lib.fa_status_string(s)
+    assert lib.fa_status_string(99)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, INVALID), ("heads", -1, INVALID), ("seqlen", 0, INVALID),
+    ("head_dim", 0, INVALID), ("head_dim", 96, UNSUPPORTED), ("head_dim", 256, UNSUPPORTED),
+    ("dtype", 7, INVALID), ("scale", float("nan"), INVALID), ("scale", float("inf"), INVALID),
+    ("scale", -0.5, INVALID), ("stride_n", 60, INVALID), ("stride_n", 36, INVALID),
+    ("stride_h", -64, INVALID), ("key_lens", 0x10004, INVALID),
+    ("seqlen", 1 << 30, UNSUPPORTED),
+])
+def test_problem_rejected_before_any_hip_call(lib, field, value, status):
+    p = prob(**{field: value})
+    assert fwd(lib, p) == status
+    assert lib.fa_last_error()
+    assert bwd(lib, p, ws_bytes=1 << 40) == status
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_null_problem(lib):
+    assert lib.fa_fwd(None, A, A, A, A, A, None) == INVALID
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+@pytest.mark.parametrize("bad", [0, A + 8])
+def test_forward_pointers(lib, which, bad):
+    kw = {which: bad}
+    assert fwd(lib, prob(), **kw) == INVALID
+    assert which in lib.fa_last_error().decode()
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"])
+def test_backward_pointers(lib, which):
+    assert bwd(lib, prob(), **{which: 0}) == INVALID
+    assert bwd(lib, prob(), **{which: A + 4}) == INVALID
+
+
+def test_workspace_size_and_too_small(lib):
+    p = prob()
+    need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+    rows = 2 * 3 * 256
+    assert need >= rows * 4 + rows * 64 * 4          # D per row + fp32 dQ accumulator
+    assert need <= rows * 4 + 256 + rows * 64 * 4    # O(N d), never O(N^2)
+    assert bwd(lib, p, ws_bytes=need - 1) == INVALID
+
+
+def test_fp32_strides_need_16_bytes(lib):
+    p = prob(dtype=_lib.FA_DTYPE_F32, stride_n=66, stride_h=256 * 66, stride_b=3 * 256 * 66)
+    assert fwd(lib, p) == INVALID
+
+
+@pytest.mark.parametrize("mb,hstride,status", [
+    (100, 0, INVALID),        # does not divide N = 256
+    (64, 0, UNSUPPORTED),     # divides N but is not a multiple of 128
+    (0, 0, INVALID),
+    (128, -1, INVALID),
+])
+def test_block_mask_arguments(lib, mb, hstride, status):
+    p = prob()
+    assert lib.fa_fwd_blocksparse(ctypes.byref(p), A, mb, hstride, A, A, A, A, A, None) == status
+    ws = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+    assert lib.fa_bwd_blocksparse(ctypes.byref(p), A, mb, hstride, A, A, A, A, A, A, A, A, A, A, ws,
+                                  None) == status
+
+
+def test_null_block_mask(lib):
+    p = prob()
+    assert lib.fa_fwd_blocksparse(ctypes.byref(p), None, 128, 0, A, A, A, A, A, None) == INVALID
+
+
+def test_too_many_mask_blocks(lib):
+    p = prob(batch=1, heads=1, seqlen=128 * 1025, stride_h=128 * 1025 * 64, stride_b=128 * 1025 * 64)
+    assert lib.fa_fwd_blocksparse(ctypes.byref(p), A, 128, 0, A, A, A, A, A, None) == UNSUPPORTED
+
+
+def test_error_message_cleared_by_next_call(lib):
+    assert fwd(lib, prob(batch=0)) == INVALID
+    assert lib.fa_last_error()
+    lib.fa_bwd_workspace_bytes(ctypes.byref(prob()))
+    assert lib.fa_last_error() == b""
+
+
+def test_python_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libfa.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()

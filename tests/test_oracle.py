@@ -407,3 +407,22 @@ def test_chunking_does_not_change_results():
     g2 = oracle.backward(q, k, v, do, 0.3, causal=True, chunk=1024)
     for x, y in zip(g1, g2):
         assert rel_err(x, y) < 1e-13
+
+
+@pytest.mark.parametrize("mi", range(len(MASKS)))
+def test_sampled_gradients_equal_full_backward(mi):
+    """The sampled-row/column evaluation used at full sizes equals the full
+    backward (which the finite-difference and autograd tests pin)."""
+    kw = dict(MASKS[mi])
+    N, d = 6, 4
+    q, k, v, do = (rand((N, d), s) for s in (31, 32, 33, 34))
+    dq, dk, dv = bwd1(q, k, v, do, 0.55, **dict(kw))
+    o, lse = fwd1(q, k, v, 0.55, **dict(kw))
+    rows, cols = np.array([0, 3, 5]), np.array([1, 2, 5])
+    o_r, lse_r, dq_r, dk_c, dv_c = oracle.gradients_sampled(
+        q, k, v, do, 0.55, rows, cols, causal=kw.get("causal", False), key_len=kw.get("key_len"),
+        block_mask=kw.get("block_mask"), mb=kw.get("mb", 128), chunk=4)
+    assert rel_err(o_r, o[rows]) < 1e-14 and rel_err(lse_r, lse[rows]) < 1e-14
+    assert np.allclose(dq_r, dq[rows], rtol=0, atol=1e-13)
+    assert np.allclose(dk_c, dk[cols], rtol=0, atol=1e-13)
+    assert np.allclose(dv_c, dv[cols], rtol=0, atol=1e-13)

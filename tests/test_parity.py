@@ -1,0 +1,279 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every comparison is element by element on the same seeded inputs: the oracle
+gets the exact float64 upcast of the rounded values the GPU reads, and the
+float32 scale the GPU uses.  Error = max|x - ref| / max|ref| per output
+tensor (LSE: the same, and -inf entries must match exactly).  Tolerances are
+1e-5 for fp32, 2e-3 for fp16 and 2e-2 for bf16 outputs and gradients.
+Outputs are pre-filled with NaN so an element the kernels never write fails.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_33_amd import (fa_bwd, fa_bwd_blocksparse, fa_fwd, fa_fwd_blocksparse)
+from exact_io_aware_33_amd.inputs import WORKLOADS, as_f64, make_inputs, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-2}
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape
+    assert not np.isnan(x).any(), "NaN in GPU output (unwritten or invalid element)"
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(x), fin), "finite/infinite pattern differs"
+    assert np.array_equal(x[~fin], ref[~fin]), "non-finite values differ"
+    if not fin.any():
+        return 0.0
+    den = float(np.max(np.abs(ref[fin])))
+    num = float(np.max(np.abs(x[fin] - ref[fin])))
+    if den == 0.0:
+        return num
+    return num / den
+
+
+def nan_like(t):
+    return torch.full_like(t, float("nan"))
+
+
+def gpu_forward(inp, dtype, scale, causal, key_lens, mb, out_nan=True):
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    kl = None if key_lens is None else key_lens.cuda()
+    o = nan_like(q)
+    lse = torch.full(q.shape[:3], float("nan"), device="cuda", dtype=torch.float32)
+    if mb is None:
+        fa_fwd(q, k, v, scale=scale, causal=causal, key_lens=kl, out=o, lse=lse)
+    else:
+        fa_fwd_blocksparse(q, k, v, inp["block_mask"].cuda(), mask_block=mb, scale=scale,
+                           causal=causal, key_lens=kl, out=o, lse=lse)
+    return (q, k, v, kl), o, lse
+
+
+def gpu_backward(dev, inp, o, lse, scale, causal, mb):
+    q, k, v, kl = dev
+    do = inp["do"].cuda()
+    dq, dk, dv = nan_like(q), nan_like(q), nan_like(q)
+    if mb is None:
+        fa_bwd(q, k, v, o, lse, do, scale=scale, causal=causal, key_lens=kl, dq=dq, dk=dk, dv=dv)
+    else:
+        fa_bwd_blocksparse(q, k, v, o, lse, do, inp["block_mask"].cuda(), mask_block=mb, scale=scale,
+                           causal=causal, key_lens=kl, dq=dq, dk=dk, dv=dv)
+    return dq, dk, dv
+
+
+def check_case(B, H, N, d, dtype, *, causal=False, lens=None, key_lens=None, mb=None, density=0.3,
+               seed=0, backward=True, scale=None, block_mask=None, tol=None):
+    say(f"case B={B} H={H} N={N} d={d} {dtype} causal={causal} lens={lens} mb={mb} seed={seed}")
+    inp = make_inputs(B, H, N, d, dtype, seed=seed, with_do=backward, lens=lens, mb=mb, density=density)
+    if key_lens is not None:
+        inp["key_lens"] = torch.tensor(key_lens, dtype=torch.int32)
+    if block_mask is not None:
+        inp["block_mask"] = torch.as_tensor(block_mask, dtype=torch.uint8)
+    scale = float(np.float32(1.0 / math.sqrt(d))) if scale is None else float(np.float32(scale))
+    tol = TOL[dtype] if tol is None else tol
+    dev, o, lse = gpu_forward(inp, dtype, scale, causal, inp["key_lens"], mb)
+    if backward:
+        dq, dk, dv = gpu_backward(dev, inp, o, lse, scale, causal, mb)
+    torch.cuda.synchronize()
+    q64, k64, v64 = (as_f64(inp[n]) for n in ("q", "k", "v"))
+    lens_np = None
+    if inp["key_lens"] is not None:
+        lens_np = np.clip(inp["key_lens"].numpy().astype(np.int64), 0, N)
+    bm = None if mb is None else inp["block_mask"].numpy()
+    kw = dict(causal=causal, key_lens=lens_np, block_mask=bm, mb=mb or 128)
+    errs = {}
+    if backward:
+        rdq, rdk, rdv, (ro, rlse, _, _) = oracle.backward(q64, k64, v64, as_f64(inp["do"]), scale,
+                                                          return_aux=True, **kw)
+        errs.update(dq=rel_err(as_f64(dq), rdq), dk=rel_err(as_f64(dk), rdk), dv=rel_err(as_f64(dv), rdv))
+    else:
+        ro, rlse = oracle.forward(q64, k64, v64, scale, **kw)
+    errs.update(o=rel_err(as_f64(o), ro), lse=rel_err(lse.cpu().numpy(), rlse))
+    say("  errors: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, f"over tolerance {tol}: {bad}"
+    return errs
+
+
+# --------------------------------------------------------------- small sweeps
+MODES = {
+    "dense": dict(),
+    "causal": dict(causal=True),
+    "padding": dict(lens=(1, 300)),
+    "causal_padding": dict(causal=True, lens=(1, 300)),
+}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("N", [1, 77, 128, 300])
+def test_forward_backward_small(dtype, d, mode, N):
+    kw = dict(MODES[mode])
+    if "lens" in kw:
+        kw["lens"] = (1, max(1, N))
+    check_case(2, 3, N, d, dtype, seed=N + d, **kw)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("mb", [128, 256])
+def test_blocksparse_small(dtype, d, causal, mb):
+    check_case(2, 2, 512, d, dtype, causal=causal, mb=mb, density=0.4, seed=mb + d)
+
+
+def test_blocksparse_with_padding_and_empty_rows():
+    nb = 4
+    m = np.ones((nb, nb), np.uint8)
+    m[1, :] = 0            # query block 1 sees nothing -> O = 0, LSE = -inf
+    m[:, 2] = 0            # key block 2 is never seen -> dK = dV = 0
+    m[3, 0] = 0
+    check_case(2, 3, 512, 64, "f16", mb=128, block_mask=m, key_lens=[400, 130])
+    check_case(2, 3, 512, 64, "bf16", mb=128, block_mask=m, causal=True, key_lens=[512, 200])
+
+
+def test_blocksparse_per_head_mask():
+    H, nb = 3, 4
+    rng = np.random.default_rng(9)
+    m = (rng.random((H, nb, nb)) < 0.5).astype(np.uint8)
+    for h in range(H):
+        np.fill_diagonal(m[h], 1)
+    check_case(1, H, 512, 64, "f16", mb=128, block_mask=m)
+    check_case(1, H, 512, 128, "bf16", mb=128, block_mask=m, causal=True)
+
+
+# ------------------------------------------------------------------ edge cases
+def test_single_token():
+    for dtype in ("f32", "f16", "bf16"):
+        check_case(1, 2, 1, 64, dtype)
+        check_case(3, 1, 1, 128, dtype, causal=True)
+
+
+def test_zero_scale_is_mean_of_visible_values():
+    check_case(2, 2, 200, 64, "f32", scale=0.0)
+    check_case(2, 2, 200, 64, "bf16", scale=0.0, causal=True)
+    check_case(2, 2, 200, 128, "f16", scale=0.0, key_lens=[3, 150])
+
+
+def test_key_lengths_zero_clamped_and_full():
+    # 0 -> every row fully masked; negative clamps to 0; > N clamps to N
+    check_case(4, 2, 150, 64, "f16", key_lens=[0, -5, 1000, 150])
+    check_case(4, 2, 150, 64, "bf16", causal=True, key_lens=[0, 1, 149, 10 ** 6])
+    check_case(2, 2, 150, 128, "f32", key_lens=[0, 77])
+
+
+def test_large_score_magnitudes():
+    """Scores of order +-100 (the max subtraction must keep exp finite).
+
+    fp32 rounds each score S with an absolute error proportional to |S|, and
+    that absolute error is the relative error of exp(S).  At scale 12 the
+    scores are 12 / (1/sqrt(64)) = 96 times those of the fp32 workload, so the
+    fp32 tolerance is scaled by 96; the 16-bit tolerances (dominated by input
+    rounding) are unchanged."""
+    check_case(1, 2, 256, 64, "f32", scale=12.0, tol=TOL["f32"] * 12.0 * math.sqrt(64))
+    check_case(1, 2, 256, 64, "bf16", scale=12.0, causal=True)
+
+
+def test_strided_bnhd_layout():
+    """[B, N, H, d] storage seen as a [B, H, N, d] view."""
+    B, H, N, d = 2, 3, 200, 64
+    inp = make_inputs(B, H, N, d, "bf16", seed=5)
+    say("case strided BNHD bf16")
+    dev = {n: inp[n].permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3) for n in ("q", "k", "v", "do")}
+    assert dev["q"].stride(2) == H * d
+    o, lse = fa_fwd(dev["q"], dev["k"], dev["v"], causal=True)
+    dq, dk, dv = fa_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=True)
+    assert o.stride() == dev["q"].stride()
+    scale = float(np.float32(1 / math.sqrt(d)))
+    rdq, rdk, rdv, (ro, rlse, _, _) = oracle.backward(*(as_f64(inp[n]) for n in ("q", "k", "v", "do")),
+                                                      scale, causal=True, return_aux=True)
+    for x, r in ((o, ro), (dq, rdq), (dk, rdk), (dv, rdv)):
+        assert rel_err(as_f64(x), r) <= TOL["bf16"]
+    assert rel_err(lse.cpu().numpy(), rlse) <= TOL["bf16"]
+
+
+def test_forward_is_bitwise_reproducible():
+    inp = make_inputs(2, 4, 1000, 64, "bf16", seed=3)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o1, l1 = fa_fwd(q, k, v, causal=True)
+    o2, l2 = fa_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------- the named workloads
+def test_workload_fp32_fwd_n256():
+    w = WORKLOADS["fp32_fwd_n256"]
+    check_case(w.B, w.H, w.N, w.d, w.dtype, backward=False)
+
+
+def test_workload_gpt2_causal_n1k():
+    w = WORKLOADS["gpt2_causal_n1k"]
+    check_case(w.B, w.H, w.N, w.d, w.dtype, causal=True)
+
+
+def test_workload_bert_padding_n512():
+    w = WORKLOADS["bert_padding_n512"]
+    check_case(w.B, w.H, w.N, w.d, w.dtype, lens=w.lens)
+
+
+def _sampled(w, heads, n_rows=192, n_cols=192, seed=0):
+    """Full-size launch; oracle on sampled rows/columns of some heads."""
+    say(f"case {w.name} full size, sampled heads {heads}")
+    inp = make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed=seed, lens=w.lens, mb=w.mb, density=w.density)
+    scale = w.scale
+    dev, o, lse = gpu_forward(inp, w.dtype, scale, w.causal, inp["key_lens"], w.mb)
+    dq, dk, dv = gpu_backward(dev, inp, o, lse, scale, w.causal, w.mb)
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv):
+        assert not torch.isnan(t).any().item(), "unwritten element"
+    rng = np.random.default_rng(1234)
+    N = w.N
+    edges = np.array([0, 1, 63, 64, 127, 128, N // 2, N - 129, N - 128, N - 2, N - 1])
+    rows = np.unique(np.concatenate([edges, rng.choice(N, n_rows, replace=False)]))
+    cols = np.unique(np.concatenate([edges, rng.choice(N, n_cols, replace=False)]))
+    bm = None if w.mb is None else inp["block_mask"].numpy()
+    tol = TOL[w.dtype]
+    for (b, h) in heads:
+        ro, rlse, rdq, rdk, rdv = oracle.gradients_sampled(
+            *(as_f64(inp[n][b, h]) for n in ("q", "k", "v", "do")), scale, rows, cols,
+            causal=w.causal, block_mask=bm, mb=w.mb or 128)
+        errs = dict(
+            o=rel_err(as_f64(o[b, h])[rows], ro), lse=rel_err(lse[b, h].cpu().numpy()[rows], rlse),
+            dq=rel_err(as_f64(dq[b, h])[rows], rdq), dk=rel_err(as_f64(dk[b, h])[cols], rdk),
+            dv=rel_err(as_f64(dv[b, h])[cols], rdv))
+        say(f"  head ({b},{h}) errors: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        bad = {n: e for n, e in errs.items() if not e <= tol}
+        assert not bad, f"over tolerance {tol}: {bad}"
+
+
+def test_workload_long_causal_n16k_sampled():
+    _sampled(WORKLOADS["long_causal_n16k"], heads=[(0, 0), (0, 15)])
+
+
+def test_workload_long_causal_n8k_d128_sampled():
+    _sampled(WORKLOADS["long_causal_n8k_d128"], heads=[(0, 3)])
+
+
+def test_workload_blocksparse_n16k_sampled():
+    _sampled(WORKLOADS["blocksparse_n16k"], heads=[(0, 0), (0, 7)])
