@@ -1,0 +1,273 @@
+"""Throughput of exact attention (forward + backward) on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: fa_fwd, then
+the backward launch sequence (preprocess, main kernel, dQ conversion) through
+fa_bwd_ex, all on torch's current stream.  Prints ONE JSON line on stdout.
+
+  value      whole-step TFLOP/s, FLOPs counted as 4*B*H*N^2*d for the forward
+             (halved when causal) and 2.5x that for the backward, over the
+             wall-clock time of the timed steps (inputs resident in HBM).
+  roofline   the kernel with the largest average duration: algorithmic FLOPs
+             of one launch (4*d per visible (query, key) pair forward, 10*d
+             backward) over its average duration from HIP events recorded on
+             the launch stream around every timed launch; peak = dense
+             bf16/fp16 MFMA 2516.6 TFLOP/s.  `traffic` comes from the
+             committed rocprofv3 counter summary when it was taken on the
+             current kernel sources, else null.
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "long_causal_n16k"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP/C++ sources that make up libfa."""
+    csrc = os.path.join(ROOT, "exact_io_aware_33_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "fa.h"), "rb").read())
+    return h.hexdigest()
+
+
+def visible_pairs(w, key_lens=None, block_mask=None) -> int:
+    """Number of (query, key) pairs no mask removes, summed over batch and heads."""
+    N = w.N
+    if w.mb is not None:
+        import numpy as np
+        bmk = np.asarray(block_mask).astype(bool)
+        if w.causal:
+            below = np.tril(bmk, -1).sum() * w.mb * w.mb
+            diag = np.diag(bmk).sum() * (w.mb * (w.mb + 1) // 2)
+            per_head = int(below + diag)
+        else:
+            per_head = int(bmk.sum()) * w.mb * w.mb
+        if key_lens is not None:
+            raise NotImplementedError("block mask combined with key padding")
+        return per_head * w.B * w.H
+    total = 0
+    for b in range(w.B):
+        L = N if key_lens is None else max(0, min(N, int(key_lens[b])))
+        if w.causal:
+            # query i sees keys 0..min(i, L-1)
+            full = min(L, N)
+            pairs = full * (full + 1) // 2 + (N - full) * full
+        else:
+            pairs = N * L
+        total += pairs * w.H
+    return total
+
+
+def traffic_from_profile(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
+def cpu_baseline(w, inputs, budget_heads=1):
+    """The oracle as it stands, timed on this host on one (batch, head) of the
+    workload (full N, forward + backward)."""
+    import numpy as np
+
+    import oracle
+    from exact_io_aware_33_amd.inputs import as_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((int(i.get("num_threads", 1)) for i in threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: fall back to the environment
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    sl = (slice(0, 1), slice(0, budget_heads))
+    q, k, v, do = (as_f64(inputs[n][sl]) for n in ("q", "k", "v", "do"))
+    lens = None if inputs["key_lens"] is None else inputs["key_lens"].numpy()[:1]
+    bm = None if inputs["block_mask"] is None else inputs["block_mask"].numpy()
+    t0 = time.perf_counter()
+    oracle.backward(q, k, v, do, w.scale, causal=w.causal, key_lens=lens, block_mask=bm,
+                    mb=w.mb or 128)
+    dt = time.perf_counter() - t0
+    flops_fwd = 4.0 * budget_heads * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    return {"value": round(3.5 * flops_fwd / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"1 batch x {budget_heads} head(s) of {w.name} (N={w.N}, d={w.d}), "
+                      f"fp64 numpy two-pass forward + analytic backward, {dt:.1f} s; "
+                      f"host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(every (batch, head) is independent, so more GPUs would split B*H with no "
+              "communication; that path is not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from exact_io_aware_33_amd import fa_fwd
+    from exact_io_aware_33_amd.inputs import WORKLOADS, make_workload_inputs
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    if not w.backward:
+        raise SystemExit(f"workload {w.name} is forward-only; bench times forward + backward")
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    inputs = make_workload_inputs(w, seed=0)
+    q, k, v, do = (inputs[n].to(dev) for n in ("q", "k", "v", "do"))
+    kl = None if inputs["key_lens"] is None else inputs["key_lens"].to(dev)
+    bm = None if inputs["block_mask"] is None else inputs["block_mask"].to(dev)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
+
+    from exact_io_aware_33_amd import (FA_BWD_DQ, FA_BWD_MAIN, FA_BWD_PRE, fa_bwd_ex,
+                                       fa_bwd_workspace_bytes, fa_fwd_blocksparse)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa_bwd_workspace_bytes(q, scale=w.scale, causal=w.causal, key_lens=kl),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    common = dict(scale=w.scale, causal=w.causal, key_lens=kl)
+
+    def fwd():
+        if bm is None:
+            fa_fwd(q, k, v, out=o, lse=lse, **common)
+        else:
+            fa_fwd_blocksparse(q, k, v, bm, mask_block=w.mb, out=o, lse=lse, **common)
+
+    def bwd(stage):
+        fa_bwd_ex(q, k, v, o, lse, do, stage, block_mask=bm, mask_block=w.mb or 128,
+                  workspace=ws, dq=dq, dk=dk, dv=dv, **common)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fwd()
+        if ev is not None:
+            ev[1].record(stream)
+        bwd(FA_BWD_PRE)
+        if ev is not None:
+            ev[2].record(stream)
+        bwd(FA_BWD_MAIN)
+        if ev is not None:
+            ev[3].record(stream)
+        bwd(FA_BWD_DQ)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    pre_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    main_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    dq_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step; fwd {fwd_ms:.3f} ms, "
+        f"bwd pre {pre_ms:.3f} / main {main_ms:.3f} / dq {dq_ms:.3f} ms")
+
+    f_fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    f_step = 3.5 * f_fwd
+    value = f_step / (ms_step * 1e-3) / 1e12
+
+    pairs = visible_pairs(w, None if inputs["key_lens"] is None else inputs["key_lens"].numpy(),
+                          None if inputs["block_mask"] is None else inputs["block_mask"].numpy())
+    kernels = {
+        "fwd_kernel": (fwd_ms, 4.0 * w.d * pairs),
+        "bwd_main_kernel": (main_ms, 10.0 * w.d * pairs),
+    }
+    name = max(kernels, key=lambda n: kernels[n][0])
+    dur_ms, alg_flops = kernels[name]
+    achieved = alg_flops / (dur_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    traffic = traffic_from_profile(w.name, name)
+
+    out = {
+        "metric": "attention TFLOP/s fwd & fwd+bwd, N=1K-16K d=64 bf16; % of MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "mask_block": w.mb, "key_padding": w.lens is not None},
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
+        "bwd_tflops": round(2.5 * f_fwd / ((pre_ms + main_ms + dq_ms) * 1e-3) / 1e12, 3),
+        "mfma_peak_frac_step": round(value / peak, 4),
+        "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
+                      "bwd_main": round(main_ms, 4), "bwd_dq": round(dq_ms, 4)},
+        "roofline": {"kernel": name, "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "flops_per_launch": alg_flops,
+                     "avg_launch_ms": round(dur_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host (cpu_baseline)...")
+        out["cpu_baseline"] = cpu_baseline(w, inputs)
+        log(f"[bench] cpu_baseline done: {out['cpu_baseline']['value']} TFLOP/s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

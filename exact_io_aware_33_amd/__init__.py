@@ -19,8 +19,12 @@ import torch
 from . import _lib
 from ._lib import FaError, FaProblem
 
-__all__ = ["fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_blocksparse",
-           "fa_bwd_workspace_bytes", "FaError", "library_path", "load_library"]
+__all__ = ["fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_ex",
+           "fa_bwd_workspace_bytes", "FaError", "library_path", "load_library",
+           "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_DQ", "FA_BWD_ALL"]
+
+FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ, FA_BWD_ALL = (_lib.FA_BWD_PRE, _lib.FA_BWD_MAIN,
+                                                  _lib.FA_BWD_DQ, _lib.FA_BWD_ALL)
 
 _DTYPES = {torch.float32: _lib.FA_DTYPE_F32, torch.float16: _lib.FA_DTYPE_F16,
            torch.bfloat16: _lib.FA_DTYPE_BF16}
@@ -164,3 +168,18 @@ def fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, *, mask_block=128, scale
                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(q)))
     return dq, dk, dv
+
+
+def fa_bwd_ex(q, k, v, o, lse, do, stages, *, block_mask=None, mask_block=128, scale=None,
+              causal=False, key_lens=None, workspace, dq, dk, dv):
+    """One or more stages of the backward launch sequence (FA_BWD_PRE, _MAIN,
+    _DQ bits), writing into caller-provided gradients and workspace.  Calls
+    fa_bwd_ex; block_mask None selects the dense path."""
+    _same_layout(q, k, v, o, do, dq, dk, dv)
+    p, kl = _problem(q, scale, causal, key_lens)
+    bm, hstride = (None, 0) if block_mask is None else _mask(block_mask, q)
+    lib = _lib.load()
+    _lib.check(lib.fa_bwd_ex(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), int(stages), _stream(q)))

@@ -11,7 +11,9 @@ FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_bwd_blocksparse", "fa_status_string", "fa_last_error", "fa_abi_version")
+           "fa_bwd_blocksparse", "fa_bwd_ex", "fa_status_string", "fa_last_error",
+           "fa_abi_version")
+FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 ABI_VERSION = 1
 
 
@@ -63,6 +65,9 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = i32
     lib.fa_bwd_blocksparse.argtypes = [pp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fa_bwd_blocksparse.restype = i32
+    lib.fa_bwd_ex.argtypes = [pp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                              ctypes.c_uint32, vp]
+    lib.fa_bwd_ex.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []

@@ -121,8 +121,10 @@ fa_status_t fwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
 fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int64_t hstride,
                      bool sparse, const void *q, const void *k, const void *v, const void *o,
                      const float *lse, const void *dout, void *dq, void *dk, void *dv, void *ws,
-                     size_t ws_bytes, void *stream) {
+                     size_t ws_bytes, unsigned stages, void *stream) {
   g_err[0] = 0;
+  if (stages == 0 || (stages & ~(unsigned)FA_BWD_ALL))
+    return fail(FA_ERR_INVALID, "stages must be a nonzero subset of FA_BWD_ALL (got %u)", stages);
   fa_status_t st;
   if ((st = check_problem(p)) != FA_OK) return st;
   if ((st = check_tensor(q, "q")) != FA_OK || (st = check_tensor(k, "k")) != FA_OK ||
@@ -154,7 +156,7 @@ fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
     a.nblk = p->seqlen / mb;
     a.mask_hstride = hstride;
   }
-  return hip_status(fa::launch_bwd(a, (fa_dtype_t)p->dtype, sparse, (hipStream_t)stream));
+  return hip_status(fa::launch_bwd(a, (fa_dtype_t)p->dtype, sparse, stages, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -183,7 +185,7 @@ fa_status_t fa_bwd(const fa_problem_t *p, const void *q, const void *k, const vo
                    const float *lse, const void *dout, void *dq, void *dk, void *dv, void *workspace,
                    size_t workspace_bytes, void *stream) {
   return bwd_impl(p, nullptr, 0, 0, false, q, k, v, o, lse, dout, dq, dk, dv, workspace,
-                  workspace_bytes, stream);
+                  workspace_bytes, FA_BWD_ALL, stream);
 }
 
 fa_status_t fa_bwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask, int32_t mask_block,
@@ -191,7 +193,15 @@ fa_status_t fa_bwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
                                const void *o, const float *lse, const void *dout, void *dq, void *dk,
                                void *dv, void *workspace, size_t workspace_bytes, void *stream) {
   return bwd_impl(p, block_mask, mask_block, mask_head_stride, true, q, k, v, o, lse, dout, dq, dk, dv,
-                  workspace, workspace_bytes, stream);
+                  workspace, workspace_bytes, FA_BWD_ALL, stream);
+}
+
+fa_status_t fa_bwd_ex(const fa_problem_t *p, const uint8_t *block_mask, int32_t mask_block,
+                      int64_t mask_head_stride, const void *q, const void *k, const void *v,
+                      const void *o, const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                      void *workspace, size_t workspace_bytes, uint32_t stages, void *stream) {
+  return bwd_impl(p, block_mask, mask_block, mask_head_stride, block_mask != nullptr, q, k, v, o, lse,
+                  dout, dq, dk, dv, workspace, workspace_bytes, stages, stream);
 }
 
 const char *fa_status_string(fa_status_t status) {

@@ -474,33 +474,42 @@ static hipError_t launch_main_t(const AttnParams &p, hipStream_t s) {
 }
 
 template <typename T, int D>
-static hipError_t launch_bwd_d(const AttnParams &p, bool sparse, hipStream_t s) {
+static hipError_t launch_bwd_d(const AttnParams &p, bool sparse, unsigned stages, hipStream_t s) {
   AttnParams a = p;
   void *args[] = {&a};
   const int64_t rows = (int64_t)p.B * p.H * p.N;
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&bwd_pre_kernel<T, D>),
-                                 dim3((unsigned)((rows + 255) / 256)), dim3(256), args, 0, s);
-  if (e != hipSuccess) return e;
-  if (sparse)
-    e = p.causal ? launch_main_t<T, D, true, true>(p, s) : launch_main_t<T, D, false, true>(p, s);
-  else
-    e = p.causal ? launch_main_t<T, D, true, false>(p, s) : launch_main_t<T, D, false, false>(p, s);
-  if (e != hipSuccess) return e;
-  const int64_t chunks = rows * (D / (16 / (int)sizeof(T)));
-  return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel<T, D>),
-                         dim3((unsigned)((chunks + 255) / 256)), dim3(256), args, 0, s);
+  hipError_t e = hipSuccess;
+  if (stages & FA_BWD_PRE) {
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&bwd_pre_kernel<T, D>),
+                        dim3((unsigned)((rows + 255) / 256)), dim3(256), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  if (stages & FA_BWD_MAIN) {
+    if (sparse)
+      e = p.causal ? launch_main_t<T, D, true, true>(p, s) : launch_main_t<T, D, false, true>(p, s);
+    else
+      e = p.causal ? launch_main_t<T, D, true, false>(p, s) : launch_main_t<T, D, false, false>(p, s);
+    if (e != hipSuccess) return e;
+  }
+  if (stages & FA_BWD_DQ) {
+    const int64_t chunks = rows * (D / (16 / (int)sizeof(T)));
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel<T, D>),
+                        dim3((unsigned)((chunks + 255) / 256)), dim3(256), args, 0, s);
+  }
+  return e;
 }
 
 template <typename T>
-static hipError_t launch_bwd_dt(const AttnParams &p, bool sparse, hipStream_t s) {
-  return p.d == 64 ? launch_bwd_d<T, 64>(p, sparse, s) : launch_bwd_d<T, 128>(p, sparse, s);
+static hipError_t launch_bwd_dt(const AttnParams &p, bool sparse, unsigned stages, hipStream_t s) {
+  return p.d == 64 ? launch_bwd_d<T, 64>(p, sparse, stages, s) : launch_bwd_d<T, 128>(p, sparse, stages, s);
 }
 
-hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s) {
+hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, unsigned stages,
+                      hipStream_t s) {
   switch (dt) {
-    case FA_DTYPE_F32: return launch_bwd_dt<float>(p, sparse, s);
-    case FA_DTYPE_F16: return launch_bwd_dt<_Float16>(p, sparse, s);
-    case FA_DTYPE_BF16: return launch_bwd_dt<__bf16>(p, sparse, s);
+    case FA_DTYPE_F32: return launch_bwd_dt<float>(p, sparse, stages, s);
+    case FA_DTYPE_F16: return launch_bwd_dt<_Float16>(p, sparse, stages, s);
+    case FA_DTYPE_BF16: return launch_bwd_dt<__bf16>(p, sparse, stages, s);
   }
   return hipErrorInvalidValue;
 }

@@ -39,7 +39,9 @@ struct AttnParams {
 // Launchers (defined in fa_fwd.hip / fa_bwd.hip).  They assume validated
 // arguments and return hipSuccess or the launch error.
 hipError_t launch_fwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s);
-hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s);
+// `stages`: bit set of FA_BWD_PRE / FA_BWD_MAIN / FA_BWD_DQ, run in that order.
+hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, unsigned stages,
+                      hipStream_t s);
 
 // Workspace layout shared by fa_api.cpp and fa_bwd.hip.
 inline size_t ws_delta_bytes(int64_t rows) { return (size_t)((rows * 4 + 255) / 256 * 256); }

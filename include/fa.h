@@ -156,6 +156,31 @@ fa_status_t fa_bwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
                                void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* Stages of the backward launch sequence (bit set for fa_bwd_ex). */
+typedef enum fa_bwd_stage {
+  FA_BWD_PRE = 1,    /* D = rowsum(dO * O) into the workspace; zero the dQ
+                        accumulator                                          */
+  FA_BWD_MAIN = 2,   /* recompute S, P per tile; write dK, dV; accumulate dQ */
+  FA_BWD_DQ = 4,     /* dQ = scale * accumulator, converted to the dtype     */
+  FA_BWD_ALL = 7
+} fa_bwd_stage_t;
+
+/* fa_bwd / fa_bwd_blocksparse with the launch sequence split into stages, so
+ * a caller can time a stage on its own or put other work between stages.
+ * block_mask == NULL selects the dense path (mask_block, mask_head_stride
+ * ignored); otherwise the arguments mean what they mean for
+ * fa_bwd_blocksparse.  `stages` is a nonzero subset of FA_BWD_ALL; the
+ * stages it names run in the order PRE, MAIN, DQ.  Calling with PRE, then
+ * MAIN, then DQ on one stream, with the same workspace, gives exactly the
+ * result of one call with FA_BWD_ALL.  Arguments a stage does not read are
+ * still checked. */
+fa_status_t fa_bwd_ex(const fa_problem_t *p, const uint8_t *block_mask,
+                      int32_t mask_block, int64_t mask_head_stride,
+                      const void *q, const void *k, const void *v,
+                      const void *o, const float *lse, const void *dout,
+                      void *dq, void *dk, void *dv, void *workspace,
+                      size_t workspace_bytes, uint32_t stages, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *fa_status_string(fa_status_t status);
 
