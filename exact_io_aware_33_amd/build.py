@@ -22,7 +22,11 @@ SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for every device compilation.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA results are kept in architectural VGPRs (not AGPRs): the softmax and
+# the rescaling read every accumulator, and AGPR-resident accumulators would
+# cost a v_accvgpr_read/write per element per tile.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -42,9 +42,14 @@ struct BwdCfg {
   static constexpr int KSTEPS = D / (2 * KPL);  // 32x32 MFMA steps over d
   static constexpr int TSTEPS = 16 / KPL;       // 32x32 MFMA steps over 32 queries
   static constexpr int NOB = D / 32;            // 32-wide d blocks of dK, dV
-  static constexpr int PITCH = D * E + 16;      // Q / dO / K row pitch in LDS
+  // LDS layouts.  Q / dO (and, during set-up, K) rows are read two ways: 16
+  // bytes per lane down 16 consecutive rows (MFMA A operand) and 4 rows x 64
+  // bytes per half-wave (transposing read).  No row padding is free of bank
+  // conflicts for both, so 16-bit rows are unpadded and their 16-byte chunks
+  // are XOR-swizzled per row (see Layout); fp32 rows are padded by 16 bytes.
+  static constexpr int PITCH = (E == 4) ? D * E + 16 : D * E;  // Q / dO / K rows
   static constexpr int QBYTES = BQ * PITCH;     // one staged Q (or dO) block
-  static constexpr int DSP = BQ * E + 16;       // dS^T row pitch (rows = keys)
+  static constexpr int DSP = (E == 4) ? BQ * E + 16 : BQ * E;  // dS^T rows (rows = keys)
   static constexpr int DBW = D / 64;            // 16-wide d blocks of dQ per wave
   static constexpr int QSTEPS = BKC / (4 * KPL);  // 16x16 MFMA steps over 128 keys
   static constexpr int CPR = D * E / 16;        // 16-byte chunks per row
@@ -54,20 +59,47 @@ struct BwdCfg {
   static_assert(4 * QBYTES == BKC * PITCH, "K tile aliases the staging buffers");
 };
 
+// Byte offset of (row, byte-in-row) in an LDS matrix with row pitch PITCH
+// whose 16-byte chunks are permuted within each row by XOR with swz(row).
+// For 16-bit data the permutations are chosen (and checked on gfx950 with the
+// LDS bank-conflict counter) so that the kernels' access patterns hit distinct
+// banks:
+//   ROWB = 128 (8 chunks): swz = 4*((r>>1)&1) + ((r>>2)&3) -- 16 consecutive
+//     rows at one chunk fall in 16 distinct 16-byte slots of 256 bytes, and 4
+//     consecutive rows (aligned to 4) at an aligned 4-chunk group fall in the
+//     4 distinct 64-byte quarters;
+//   ROWB = 256 (16 chunks): swz = 4*(r&3) + ((r>>2)&3), same two properties;
+//   ROWB = 64 (dS^T, 4 chunks): swz = 2*((r>>3)&1) + ((r>>2)&1) -- rows
+//     {0..3, 8..11} (+4) read as aligned 2-chunk pairs fall in 8 distinct
+//     32-byte slots.
+// SWZ = false: plain rows (fp32 data, padded pitch).
+template <int PITCH, int ROWB, bool SWZ>
+struct Layout {
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (!SWZ) return 0;
+    else if constexpr (ROWB == 128) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    else if constexpr (ROWB == 256) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return 2 * ((r >> 3) & 1) + ((r >> 2) & 1);
+  }
+  static __device__ __forceinline__ int off(int row, int byte) {
+    return row * PITCH + (byte ^ (swz(row) << 4));
+  }
+};
+
 // Element e of MFMA step t in register order, from an LDS matrix with rows =
 // contraction index: M[row0 + reg_row(KPL*t + e, h)][col0 + l32].
-template <typename T, int PITCH>
+template <typename T, typename L>
 __device__ __forceinline__ typename Mma<T>::frag regorder_frag(const char *lds, int row0, int t, int col0) {
   const int lane = threadIdx.x & 63;
   if constexpr (Mma<T>::KPL == 1) {
     const int row = row0 + reg_row(t, lane >> 5);
-    return *reinterpret_cast<const float *>(lds + row * PITCH + (col0 + (lane & 31)) * 4);
+    return *reinterpret_cast<const float *>(lds + L::off(row, (col0 + (lane & 31)) * 4));
   } else {
     const int g = lane >> 4, s16 = lane & 15;
     const int r = row0 + 16 * t + 4 * (g >> 1) + (s16 >> 2);
     const int col = col0 + 16 * (g & 1) + 4 * (s16 & 3);
-    const i16x4 lo = lds_tr4(lds, r * PITCH + col * 2);
-    const i16x4 hi = lds_tr4(lds, (r + 8) * PITCH + col * 2);
+    const i16x4 lo = lds_tr4(lds, L::off(r, col * 2));
+    const i16x4 hi = lds_tr4(lds, L::off(r + 8, col * 2));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(typename Mma<T>::frag, v);
@@ -77,18 +109,18 @@ __device__ __forceinline__ typename Mma<T>::frag regorder_frag(const char *lds, 
 // 16x16 operand in natural order from an LDS matrix whose rows are the
 // contraction index: lane (g = lane/16, i = lane%16) gets
 // M[row0 + KPL*g + e][col0 + i], e < KPL.
-template <typename T, int PITCH>
+template <typename T, typename L>
 __device__ __forceinline__ typename Mma<T>::frag colfrag16(const char *lds, int row0, int col0) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   if constexpr (Mma<T>::KPL == 1) {
-    return *reinterpret_cast<const float *>(lds + (row0 + g) * PITCH + (col0 + (lane & 15)) * 4);
+    return *reinterpret_cast<const float *>(lds + L::off(row0 + g, (col0 + (lane & 15)) * 4));
   } else {
     const int s16 = lane & 15;
     const int r = row0 + 8 * g + (s16 >> 2);
     const int col = col0 + 4 * (s16 & 3);
-    const i16x4 lo = lds_tr4(lds, r * PITCH + col * 2);
-    const i16x4 hi = lds_tr4(lds, (r + 4) * PITCH + col * 2);
+    const i16x4 lo = lds_tr4(lds, L::off(r, col * 2));
+    const i16x4 hi = lds_tr4(lds, L::off(r + 4, col * 2));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(typename Mma<T>::frag, v);
@@ -155,7 +187,9 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   using C = BwdCfg<T, D>;
   using M = Mma<T>;
   using frag = typename M::frag;
-  constexpr int KPL = C::KPL, PITCH = C::PITCH, E = C::E;
+  constexpr int KPL = C::KPL, E = C::E;
+  using LQ = Layout<C::PITCH, D * E, E != 4>;    // Q / dO / K tiles
+  using LS = Layout<C::DSP, C::BQ * E, E != 4>;  // dS^T
 
   // stage[buf][0=Q,1=dO][BQ rows]; the K tile aliases it during set-up.
   __shared__ __attribute__((aligned(16))) char stage[4 * C::QBYTES];
@@ -276,7 +310,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
       const int kk = k0 + row;
       u32x4 v = u32x4{0, 0, 0, 0};
       if (kk < N) v = ldg16(reinterpret_cast<const char *>(K + (int64_t)kk * p.sn) + col * 16);
-      *reinterpret_cast<u32x4 *>(stage + row * PITCH + col * 16) = v;
+      *reinterpret_cast<u32x4 *>(stage + LQ::off(row, col * 16)) = v;
     }
   }
   frag kf[C::KSTEPS], vf[C::KSTEPS];
@@ -302,57 +336,65 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   for (int db = 0; db < C::DBW; ++db)
 #pragma unroll
     for (int st = 0; st < C::QSTEPS; ++st)
-      kq[db][st] = colfrag16<T, PITCH>(stage, st * 4 * KPL, (wave * C::DBW + db) * 16);
+      kq[db][st] = colfrag16<T, LQ>(stage, st * 4 * KPL, (wave * C::DBW + db) * 16);
   __syncthreads();  // the staging buffers are reused from here on
 
-  // ---- query-block staging: global -> registers -> LDS (double buffer)
+  // ---- query-block staging: buffer loads -> registers -> LDS (double
+  // buffer).  Lane offsets inside a block are loop invariant, the block start
+  // goes in the scalar offset, and rows past N read as zeros.
+  const uint32_t q_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, q_bytes);
+  const __amdgpu_buffer_rsrc_t dors = make_rsrc(dO, q_bytes);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(LSE, (uint32_t)N * 4u);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(Dl, (uint32_t)N * 4u);
+  const int row_bytes = (int)(p.sn * E);
+  int voff[C::CPTQ];
+#pragma unroll
+  for (int u = 0; u < C::CPTQ; ++u) {
+    const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+    voff[u] = row * row_bytes + col * 16;
+  }
   u32x4 sq[C::CPTQ], sdo[C::CPTQ];
   float slse = 0.f, sdel = 0.f;
   auto load_q = [&](int q0) {
+    const int so = q0 * row_bytes;
 #pragma unroll
     for (int u = 0; u < C::CPTQ; ++u) {
-      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-      const int qq = q0 + row;
-      if (qq < N) {
-        sq[u] = ldg16(reinterpret_cast<const char *>(Q + (int64_t)qq * p.sn) + col * 16);
-        sdo[u] = ldg16(reinterpret_cast<const char *>(dO + (int64_t)qq * p.sn) + col * 16);
-      } else {
-        sq[u] = u32x4{0, 0, 0, 0};
-        sdo[u] = u32x4{0, 0, 0, 0};
-      }
+      sq[u] = buf_load16(qrs, voff[u], so);
+      sdo[u] = buf_load16(dors, voff[u], so);
     }
     if (tid < C::BQ) {
-      const int qq = q0 + tid;
-      // rows past N, and rows that see no key (LSE = -inf), get P = 0
-      slse = INFINITY;
-      sdel = 0.f;
-      if (qq < N) {
-        const float l = LSE[qq];
-        slse = (l == -INFINITY) ? INFINITY : l * kLog2e;
-        sdel = Dl[qq];
-      }
+      const int so4 = __builtin_amdgcn_readfirstlane(q0 * 4);
+      slse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, tid * 4, so4, 0));
+      sdel = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(drs, tid * 4, so4, 0));
     }
   };
-  auto store_q = [&](int buf) {
+  auto store_q = [&](int buf, int q0) {
     char *ql = stage + buf * 2 * C::QBYTES;
     char *dl = ql + C::QBYTES;
 #pragma unroll
     for (int u = 0; u < C::CPTQ; ++u) {
       const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-      *reinterpret_cast<u32x4 *>(ql + row * PITCH + col * 16) = sq[u];
-      *reinterpret_cast<u32x4 *>(dl + row * PITCH + col * 16) = sdo[u];
+      *reinterpret_cast<u32x4 *>(ql + LQ::off(row, col * 16)) = sq[u];
+      *reinterpret_cast<u32x4 *>(dl + LQ::off(row, col * 16)) = sdo[u];
     }
     if (tid < C::BQ) {
-      lsed[buf][0][tid] = slse;
-      lsed[buf][1][tid] = sdel;
+      // rows past N, and rows that see no key (LSE = -inf), get P = 0
+      const bool in = q0 + tid < N;
+      lsed[buf][0][tid] = (!in || slse == -INFINITY) ? INFINITY : slse * kLog2e;
+      lsed[buf][1][tid] = in ? sdel : 0.f;
     }
   };
 
   const float c2 = p.scale_log2;
   if (nq > 0) {
     load_q(qblock_start(0));
-    store_q(0);
+    store_q(0, qblock_start(0));
   }
+  // Retire every outstanding load (K/V operands included) on all paths into
+  // the loop, so the compiler does not wait on the next block's prefetch
+  // inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int it = 0; it < nq; ++it) {
@@ -371,7 +413,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int st = 0; st < C::KSTEPS; ++st) {
-        const int off = l32 * PITCH + (h * (D / 2) + st * KPL) * E;
+        const int off = LQ::off(l32, (h * (D / 2) + st * KPL) * E);
         s = M::mma32(lds_frag<T>(ql, off), kf[st], s);
         dp = M::mma32(lds_frag<T>(dl, off), vf[st], dp);
       }
@@ -401,15 +443,15 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
         const frag sb = pack_frag<T>(dp, t * KPL);
 #pragma unroll
         for (int nb = 0; nb < C::NOB; ++nb) {
-          dvacc[nb] = M::mma32(regorder_frag<T, PITCH>(dl, 0, t, nb * 32), pb, dvacc[nb]);
-          dkacc[nb] = M::mma32(regorder_frag<T, PITCH>(ql, 0, t, nb * 32), sb, dkacc[nb]);
+          dvacc[nb] = M::mma32(regorder_frag<T, LQ>(dl, 0, t, nb * 32), pb, dvacc[nb]);
+          dkacc[nb] = M::mma32(regorder_frag<T, LQ>(ql, 0, t, nb * 32), sb, dkacc[nb]);
         }
       }
       // dS^T -> LDS: row = key (this lane), 4 consecutive queries per group
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qc = 8 * i + 4 * h;
-        char *dst = dsl + (32 * wave + l32) * C::DSP + qc * E;
+        char *dst = dsl + LS::off(32 * wave + l32, qc * E);
         if constexpr (E == 4) {
           *reinterpret_cast<f32x4 *>(dst) = f32x4{dp[4 * i], dp[4 * i + 1], dp[4 * i + 2], dp[4 * i + 3]};
         } else {
@@ -423,7 +465,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        char *dst = dsl + (32 * wave + l32) * C::DSP + (8 * i + 4 * h) * E;
+        char *dst = dsl + LS::off(32 * wave + l32, (8 * i + 4 * h) * E);
         if constexpr (E == 4) {
           *reinterpret_cast<f32x4 *>(dst) = f32x4{0.f, 0.f, 0.f, 0.f};
         } else {
@@ -431,7 +473,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
         }
       }
     }
-    if (has_next) store_q(buf ^ 1);
+    if (has_next) store_q(buf ^ 1, qblock_start(it + 1));
     __syncthreads();
 
     // dQ[q0 .. q0+31][wave's d slice] += dS K over the workgroup's keys
@@ -442,7 +484,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
       for (int db = 0; db < C::DBW; ++db) acc[db] = f32x4{};
 #pragma unroll
       for (int st = 0; st < C::QSTEPS; ++st) {
-        const frag a = colfrag16<T, C::DSP>(dsl, st * 4 * KPL, qh * 16);
+        const frag a = colfrag16<T, LS>(dsl, st * 4 * KPL, qh * 16);
 #pragma unroll
         for (int db = 0; db < C::DBW; ++db) acc[db] = M::mma16(a, kq[db][st], acc[db]);
       }

@@ -96,12 +96,50 @@ __device__ __forceinline__ typename Mma<T>::frag pack_frag(const f32x16 &acc, in
   }
 }
 
+// Sum of the KPL elements of an MFMA operand, added to `acc` (v_dot2 with ones
+// for 16-bit types: the sum of exactly the rounded values the MFMA consumes).
+template <typename T>
+__device__ __forceinline__ float frag_sum(typename Mma<T>::frag f, float acc) {
+  if constexpr (Mma<T>::KPL == 1) {
+    return acc + f;
+  } else if constexpr (__is_same(T, __bf16)) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 v = {f[e], f[e + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
+    }
+    return acc;
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const f16x2 v = {f[e], f[e + 1]};
+      acc = __builtin_amdgcn_fdot2(v, one, acc, false);
+    }
+    return acc;
+  }
+}
+
 // ---- global memory -----------------------------------------------------------
 __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 __device__ __forceinline__ void stg16(void *p, u32x4 v) {
   *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// Buffer resource over `bytes` bytes from `base` (raw buffer, stride 0):
+// loads past the end return zeros, which is how rows >= N are zero-filled.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset voffset + soffset (soffset wave-uniform).
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       r, voffset, __builtin_amdgcn_readfirstlane(soffset), 0));
 }
 
 // ---- LDS reads ---------------------------------------------------------------

@@ -25,6 +25,8 @@
 // the B operand of O^T += V^T P^T.  V^T fragments come from the row-major V
 // tile in LDS through the transposing LDS read (ds_read_b64_tr_b16).
 // Exponentials are base 2 with scale*log2(e) folded into one FMA.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -41,8 +43,15 @@ struct FwdCfg {
   static constexpr int NOB = D / 32;              // 32-wide blocks of the output
   static constexpr int KSTEPS = D / (2 * KPL);    // MFMA steps over d
   static constexpr int PSTEPS = 16 / KPL;         // MFMA steps over 32 keys
-  static constexpr int PITCH = D * E + 16;        // LDS row pitch (bytes)
-  static constexpr int TILE_BYTES = BC * PITCH;
+  // LDS row pitches, chosen so that the reads of each tile are free of bank
+  // conflicts (measured on gfx950): K rows are read 16 bytes per lane down 16
+  // consecutive rows (pitch = 16 mod 32 bytes); V rows are read by the
+  // transposing read, 4 rows x 64 bytes per half-wave (pitch = 64 mod 256).
+  static constexpr int PITCH = D * E + 16;        // K tile row pitch (bytes)
+  static constexpr int VPITCH = (E == 4) ? D * E + 16 : D * E + 64;  // V tile row pitch
+  static constexpr int KTILE = BC * PITCH;
+  static constexpr int VTILE = BC * VPITCH;
+  static constexpr int TILE_BYTES = KTILE + VTILE;  // one stage: K then V
   static constexpr int CPR = D * E / 16;          // 16-byte chunks per row
   static constexpr int CPT = BC * CPR / (64 * WAVES);  // chunks per thread
   static_assert(BC * CPR % (64 * WAVES) == 0, "tile must split evenly");
@@ -77,7 +86,7 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   using frag = typename M::frag;
   constexpr int KPL = C::KPL, PITCH = C::PITCH, E = C::E;
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::TILE_BYTES];
   __shared__ uint16_t blist[SPARSE ? kMaxMaskBlocks : 1];
   __shared__ int nlist_s;
 
@@ -155,30 +164,36 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
     for (int s = 0; s < C::KSTEPS; ++s) qf[s] = frag{};
   }
 
-  // ---- K/V staging: global -> registers (next tile) -> LDS (double buffer)
+  // ---- K/V staging: buffer loads (next tile) -> registers -> LDS (double
+  // buffer).  Lane offsets inside a tile are loop invariant; the tile start
+  // goes in the scalar offset, and rows past N read as zeros.
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, kv_bytes);
+  const int row_bytes = (int)(p.sn * E);
+  int voff[C::CPT];
+#pragma unroll
+  for (int u = 0; u < C::CPT; ++u) {
+    const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+    voff[u] = row * row_bytes + col * 16;
+  }
   u32x4 stk[C::CPT], stv[C::CPT];
   auto load_tile = [&](int kv0) {
+    const int so = kv0 * row_bytes;
 #pragma unroll
     for (int u = 0; u < C::CPT; ++u) {
-      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-      const int key = kv0 + row;
-      if (key < N) {
-        stk[u] = ldg16(reinterpret_cast<const char *>(K + (int64_t)key * p.sn) + col * 16);
-        stv[u] = ldg16(reinterpret_cast<const char *>(V + (int64_t)key * p.sn) + col * 16);
-      } else {
-        stk[u] = u32x4{0, 0, 0, 0};
-        stv[u] = u32x4{0, 0, 0, 0};
-      }
+      stk[u] = buf_load16(krs, voff[u], so);
+      stv[u] = buf_load16(vrs, voff[u], so);
     }
   };
   auto store_tile = [&](int buf) {
-    char *kl = smem + buf * 2 * C::TILE_BYTES;
-    char *vl = kl + C::TILE_BYTES;
+    char *kl = smem + buf * C::TILE_BYTES;
+    char *vl = kl + C::KTILE;
 #pragma unroll
     for (int u = 0; u < C::CPT; ++u) {
       const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
       *reinterpret_cast<u32x4 *>(kl + row * PITCH + col * 16) = stk[u];
-      *reinterpret_cast<u32x4 *>(vl + row * PITCH + col * 16) = stv[u];
+      *reinterpret_cast<u32x4 *>(vl + row * C::VPITCH + col * 16) = stv[u];
     }
   };
 
@@ -189,85 +204,112 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   for (int nb = 0; nb < C::NOB; ++nb) oacc[nb] = f32x16{};
   const float c2 = p.scale_log2;
 
-  if (ntiles > 0) {
-    load_tile(tile_start(0));
-    store_tile(0);
+  // Tiles that no mask touches form a prefix of the list (tiles ascend): a key
+  // tile is whole for every query of the workgroup when it ends at or before
+  // the padding length and (causal) at or before the tile's first query.
+  const int lim = CAUSAL ? min(kv_len, q_tile0 + 1) : kv_len;
+  int n_full;
+  if constexpr (SPARSE) {
+    n_full = 0;
+    for (int bi = 0; bi * tiles_per_blk < ntiles; ++bi) {
+      const int f = min(tiles_per_blk, max(0, (lim - (int)blist[bi] * p.mb) / C::BC));
+      n_full += f;
+      if (f < tiles_per_blk) break;
+    }
+    n_full = min(n_full, ntiles);
+  } else {
+    n_full = min(ntiles, lim / C::BC);
   }
-  __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int kv0 = tile_start(it);
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(tile_start(it + 1));
-    const char *kl = smem + (it & 1) * 2 * C::TILE_BYTES;
-    const char *vl = kl + C::TILE_BYTES;
-
-    const bool skip = CAUSAL && kv0 > qw0 + 31;  // tile invisible to this wave
-    if (!skip) {
-      // step 1: S^T = K_j Q_i^T
-      f32x16 sacc[C::NSB];
+  // One key tile: scores, (masking), running max / rescale, exp, PV.
+  auto tile = [&](const char *kl, const char *vl, int kv0, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    // step 1: S^T = K_j Q_i^T
+    f32x16 sacc[C::NSB];
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) {
-        sacc[sb] = f32x16{};
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      sacc[sb] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-          const frag a = lds_frag<T>(kl, (sb * 32 + l32) * PITCH + (h * (D / 2) + s * KPL) * E);
-          sacc[sb] = M::mma32(a, qf[s], sacc[sb]);
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        const frag a = lds_frag<T>(kl, (sb * 32 + l32) * PITCH + (h * (D / 2) + s * KPL) * E);
+        sacc[sb] = M::mma32(a, qf[s], sacc[sb]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (MASK) {
+          const int key = kv0 + sb * 32 + reg_row(r, h);
+          if (!(key < kv_len && (!CAUSAL || key <= qi))) sacc[sb][r] = -INFINITY;
         }
+        mx = fmaxf(mx, sacc[sb][r]);
       }
-      // masking of boundary tiles (padding / ragged end / causal diagonal)
-      const bool need_mask = (kv0 + C::BC > kv_len) || (CAUSAL && kv0 + C::BC - 1 > qw0);
-      float mx = -INFINITY;
-      if (need_mask) {
-#pragma unroll
-        for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + sb * 32 + reg_row(r, h);
-            const bool ok = key < kv_len && (!CAUSAL || key <= qi);
-            if (!ok) sacc[sb][r] = -INFINITY;
-            mx = fmaxf(mx, sacc[sb][r]);
-          }
-      } else {
-#pragma unroll
-        for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      }
-      // steps 2-3: running max and rescale of the carried state
-      mx = fmaxf(mx, xor32(mx));
-      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    // steps 2-3: running max; the carried state is rescaled only when some
+    // lane's max grew (exp2(0) = 1 for the others)
+    mx = fmaxf(mx, xor32(mx));
+    const float mt = (MASK && mx == -INFINITY) ? -INFINITY : mx * c2;
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (MASK && m_new == -INFINITY) ? 0.f : m_new;
+    if (__ballot(m_new > m_run) != 0) {
       const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int nb = 0; nb < C::NOB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
-      float lsum = 0.f;
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = fast_exp2(fmaf(sacc[sb][r], c2, -m_use));
-          if (need_mask && sacc[sb][r] == -INFINITY) x = 0.f;
-          sacc[sb][r] = x;
-          lsum += x;
-        }
-      l_run += lsum;
-      // step 4: O_i^T += V_j^T P^T
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-        for (int t = 0; t < C::PSTEPS; ++t) {
-          const frag pb = pack_frag<T>(sacc[sb], t * KPL);
-#pragma unroll
-          for (int nb = 0; nb < C::NOB; ++nb)
-            oacc[nb] = M::mma32(vt_frag<T, PITCH>(vl, sb, t, nb), pb, oacc[nb]);
-        }
     }
+    m_run = m_new;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = fast_exp2(fmaf(sacc[sb][r], c2, -m_use));
+        if constexpr (MASK) {
+          if (sacc[sb][r] == -INFINITY) x = 0.f;
+        }
+        sacc[sb][r] = x;
+      }
+    // step 4: O_i^T += V_j^T P^T; the row sum takes the same rounded P
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+      for (int t = 0; t < C::PSTEPS; ++t) {
+        const frag pb = pack_frag<T>(sacc[sb], t * KPL);
+        l_run = frag_sum<T>(pb, l_run);
+#pragma unroll
+        for (int nb = 0; nb < C::NOB; ++nb)
+          oacc[nb] = M::mma32(vt_frag<T, C::VPITCH>(vl, sb, t, nb), pb, oacc[nb]);
+      }
+  };
+
+  if (ntiles > 0) {
+    load_tile(tile_start(0));
+    store_tile(0);
+  }
+  // Retire every outstanding load (Q fragments included) on all paths into
+  // the loop; otherwise the compiler keeps them "pending" at the loop header
+  // and waits on the next tile's prefetch before the first MFMA of each tile.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  int it = 0;
+  for (; it < n_full; ++it) {
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(tile_start(it + 1));
+    const char *kl = smem + (it & 1) * C::TILE_BYTES;
+    tile(kl, kl + C::KTILE, tile_start(it), std::integral_constant<bool, false>{});
+    if (has_next) store_tile((it + 1) & 1);
+    __syncthreads();
+  }
+  for (; it < ntiles; ++it) {
+    const int kv0 = tile_start(it);
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(tile_start(it + 1));
+    const char *kl = smem + (it & 1) * C::TILE_BYTES;
+    if (!(CAUSAL && kv0 > qw0 + 31))  // some key of the tile is visible to this wave
+      tile(kl, kl + C::KTILE, kv0, std::integral_constant<bool, true>{});
     if (has_next) store_tile((it + 1) & 1);
     __syncthreads();
   }
