@@ -135,7 +135,7 @@ fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
     return st;
   if (sparse && (st = check_mask(p, mask, mb, hstride)) != FA_OK) return st;
   const int64_t rows = (int64_t)p->batch * p->heads * p->seqlen;
-  const size_t need = fa::ws_total_bytes(rows, p->head_dim);
+  const size_t need = fa::ws_total_bytes(rows);
   if (ws_bytes < need)
     return fail(FA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
   fa::AttnParams a = make_params(p);
@@ -149,7 +149,6 @@ fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
   a.dk = dk;
   a.dv = dv;
   a.ws_delta = static_cast<float *>(ws);
-  a.ws_dq = reinterpret_cast<float *>(static_cast<char *>(ws) + fa::ws_delta_bytes(rows));
   if (sparse) {
     a.mask = mask;
     a.mb = mb;
@@ -178,7 +177,7 @@ size_t fa_bwd_workspace_bytes(const fa_problem_t *p) {
   g_err[0] = 0;
   if (check_problem(p) != FA_OK) return 0;
   const int64_t rows = (int64_t)p->batch * p->heads * p->seqlen;
-  return fa::ws_total_bytes(rows, p->head_dim);
+  return fa::ws_total_bytes(rows);
 }
 
 fa_status_t fa_bwd(const fa_problem_t *p, const void *q, const void *k, const void *v, const void *o,

@@ -11,20 +11,25 @@
 // Block-sparse section of the same page: zero mask blocks are skipped here too.
 //
 // Kernels (all on the caller's stream):
-//  1. bwd_pre:   D = rowsum(dO * O) per query row, and zero the fp32 dQ
-//                accumulator (a fill kernel, no memset node).
-//  2. bwd_main:  one workgroup per (batch, head, 128-key tile), one wavefront
-//                per 32 keys.  K and V rows of the wave stay in registers;
-//                query blocks of 32 rows (Q, dO, LSE, D) stream through LDS,
-//                double buffered.  Per block: S = Q K^T and dP = dO V^T on
-//                32x32 MFMAs (scores in "register order", rows = queries), P
-//                and dS in fp32, then dV^T += dO^T P and dK^T += Q^T dS with
-//                P, dS fed back from registers, dO^T / Q^T from LDS through
-//                the transposing read.  dS^T goes to LDS; after one barrier
-//                every wave computes a 32 x d/4 slice of dQ = dS K over the
-//                workgroup's 128 keys on 16x16 MFMAs and adds it into the
-//                fp32 accumulator with global float atomics.
-//  3. bwd_dq:    dQ = scale * accumulator, converted to the storage dtype.
+//  1. bwd_pre:   D = rowsum(dO * O) per query row (the only workspace: one
+//                float per row, O(N) extra memory).
+//  2. bwd_main:  dK and dV.  One workgroup per (batch, head, 128-key tile), one
+//                wavefront per 32 keys; K and V rows of the wave stay in
+//                registers, query blocks of 32 rows (Q, dO, LSE, D) stream
+//                through LDS.  Per block: S = Q K^T and dP = dO V^T on 32x32
+//                MFMAs (rows = queries in register order), P and dS in fp32,
+//                then dV^T += dO^T P and dK^T += Q^T dS with P and dS fed back
+//                from registers and dO^T / Q^T read through the transposing
+//                LDS read.
+//  3. bwd_dq:    dQ.  One workgroup per (batch, head, 128-query tile), laid out
+//                like the forward: each lane owns one query; S^T = K Q^T and
+//                dP^T = V dO^T per key tile, dS^T in registers, then
+//                dQ^T += K^T dS^T with K^T read through the transposing LDS
+//                read.  dQ is written once per row: no atomics, and the result
+//                does not depend on scheduling.
+// bwd_main and bwd_dq both read D and are independent of each other.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -32,103 +37,8 @@ namespace fa {
 
 constexpr int kMaxMaskBlocksB = 1024;
 
-template <typename T, int D>
-struct BwdCfg {
-  static constexpr int E = sizeof(T);
-  static constexpr int KPL = Mma<T>::KPL;
-  static constexpr int WAVES = 4;
-  static constexpr int BKC = 32 * WAVES;        // keys per workgroup
-  static constexpr int BQ = 32;                 // queries per iteration
-  static constexpr int KSTEPS = D / (2 * KPL);  // 32x32 MFMA steps over d
-  static constexpr int TSTEPS = 16 / KPL;       // 32x32 MFMA steps over 32 queries
-  static constexpr int NOB = D / 32;            // 32-wide d blocks of dK, dV
-  // LDS layouts.  Q / dO (and, during set-up, K) rows are read two ways: 16
-  // bytes per lane down 16 consecutive rows (MFMA A operand) and 4 rows x 64
-  // bytes per half-wave (transposing read).  No row padding is free of bank
-  // conflicts for both, so 16-bit rows are unpadded and their 16-byte chunks
-  // are XOR-swizzled per row (see Layout); fp32 rows are padded by 16 bytes.
-  static constexpr int PITCH = (E == 4) ? D * E + 16 : D * E;  // Q / dO / K rows
-  static constexpr int QBYTES = BQ * PITCH;     // one staged Q (or dO) block
-  static constexpr int DSP = (E == 4) ? BQ * E + 16 : BQ * E;  // dS^T rows (rows = keys)
-  static constexpr int DBW = D / 64;            // 16-wide d blocks of dQ per wave
-  static constexpr int QSTEPS = BKC / (4 * KPL);  // 16x16 MFMA steps over 128 keys
-  static constexpr int CPR = D * E / 16;        // 16-byte chunks per row
-  static constexpr int CPTQ = BQ * CPR / (64 * WAVES);   // staged chunks / thread / tensor
-  static constexpr int CPTK = BKC * CPR / (64 * WAVES);  // K-tile chunks / thread
-  static_assert(BQ * CPR % (64 * WAVES) == 0, "query block must split evenly");
-  static_assert(4 * QBYTES == BKC * PITCH, "K tile aliases the staging buffers");
-};
-
-// Byte offset of (row, byte-in-row) in an LDS matrix with row pitch PITCH
-// whose 16-byte chunks are permuted within each row by XOR with swz(row).
-// For 16-bit data the permutations are chosen (and checked on gfx950 with the
-// LDS bank-conflict counter) so that the kernels' access patterns hit distinct
-// banks:
-//   ROWB = 128 (8 chunks): swz = 4*((r>>1)&1) + ((r>>2)&3) -- 16 consecutive
-//     rows at one chunk fall in 16 distinct 16-byte slots of 256 bytes, and 4
-//     consecutive rows (aligned to 4) at an aligned 4-chunk group fall in the
-//     4 distinct 64-byte quarters;
-//   ROWB = 256 (16 chunks): swz = 4*(r&3) + ((r>>2)&3), same two properties;
-//   ROWB = 64 (dS^T, 4 chunks): swz = 2*((r>>3)&1) + ((r>>2)&1) -- rows
-//     {0..3, 8..11} (+4) read as aligned 2-chunk pairs fall in 8 distinct
-//     32-byte slots.
-// SWZ = false: plain rows (fp32 data, padded pitch).
-template <int PITCH, int ROWB, bool SWZ>
-struct Layout {
-  static __device__ __forceinline__ int swz(int r) {
-    if constexpr (!SWZ) return 0;
-    else if constexpr (ROWB == 128) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-    else if constexpr (ROWB == 256) return 4 * (r & 3) + ((r >> 2) & 3);
-    else return 2 * ((r >> 3) & 1) + ((r >> 2) & 1);
-  }
-  static __device__ __forceinline__ int off(int row, int byte) {
-    return row * PITCH + (byte ^ (swz(row) << 4));
-  }
-};
-
-// Element e of MFMA step t in register order, from an LDS matrix with rows =
-// contraction index: M[row0 + reg_row(KPL*t + e, h)][col0 + l32].
-template <typename T, typename L>
-__device__ __forceinline__ typename Mma<T>::frag regorder_frag(const char *lds, int row0, int t, int col0) {
-  const int lane = threadIdx.x & 63;
-  if constexpr (Mma<T>::KPL == 1) {
-    const int row = row0 + reg_row(t, lane >> 5);
-    return *reinterpret_cast<const float *>(lds + L::off(row, (col0 + (lane & 31)) * 4));
-  } else {
-    const int g = lane >> 4, s16 = lane & 15;
-    const int r = row0 + 16 * t + 4 * (g >> 1) + (s16 >> 2);
-    const int col = col0 + 16 * (g & 1) + 4 * (s16 & 3);
-    const i16x4 lo = lds_tr4(lds, L::off(r, col * 2));
-    const i16x4 hi = lds_tr4(lds, L::off(r + 8, col * 2));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(typename Mma<T>::frag, v);
-  }
-}
-
-// 16x16 operand in natural order from an LDS matrix whose rows are the
-// contraction index: lane (g = lane/16, i = lane%16) gets
-// M[row0 + KPL*g + e][col0 + i], e < KPL.
-template <typename T, typename L>
-__device__ __forceinline__ typename Mma<T>::frag colfrag16(const char *lds, int row0, int col0) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
-  if constexpr (Mma<T>::KPL == 1) {
-    return *reinterpret_cast<const float *>(lds + L::off(row0 + g, (col0 + (lane & 15)) * 4));
-  } else {
-    const int s16 = lane & 15;
-    const int r = row0 + 8 * g + (s16 >> 2);
-    const int col = col0 + 4 * (s16 & 3);
-    const i16x4 lo = lds_tr4(lds, L::off(r, col * 2));
-    const i16x4 hi = lds_tr4(lds, L::off(r + 4, col * 2));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(typename Mma<T>::frag, v);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O); zero the dQ accumulator.  One thread per row.
+// 1. D = rowsum(dO * O).  One thread per row.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(AttnParams p) {
   const int64_t rows = (int64_t)p.B * p.H * p.N;
@@ -152,49 +62,41 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(AttnParams p) {
     for (int e = 0; e < EPC; ++e) acc = fmaf((float)ta[e], (float)tb[e], acc);
   }
   p.ws_delta[row] = acc;
-  float *dq = p.ws_dq + row * D;
-#pragma unroll
-  for (int c = 0; c < D / 4; ++c) reinterpret_cast<f32x4 *>(dq)[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ = scale * accumulator -> storage dtype.  One thread per 16 output bytes.
+// 2. dK, dV (key-stationary).
 template <typename T, int D>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
-  constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int CPR = D / EPC;
-  const int64_t total = (int64_t)p.B * p.H * p.N * CPR;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= total) return;
-  const int64_t row = id / CPR;
-  const int c = (int)(id % CPR);
-  const int n = (int)(row % p.N);
-  const int64_t bh = row / p.N;
-  const int b = (int)(bh / p.H), hh = (int)(bh % p.H);
-  const float *src = p.ws_dq + row * D + c * EPC;
-  T *dst = static_cast<T *>(p.dq) + (int64_t)b * p.sb + (int64_t)hh * p.sh + (int64_t)n * p.sn + c * EPC;
-  u32x4 out;
-  T *to = reinterpret_cast<T *>(&out);
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) to[e] = (T)(src[e] * p.scale);
-  stg16(dst, out);
-}
+struct BwdCfg {
+  static constexpr int E = sizeof(T);
+  static constexpr int KPL = Mma<T>::KPL;
+  static constexpr int WAVES = 4;
+  static constexpr int BKC = 32 * WAVES;        // keys per workgroup
+  static constexpr int BQ = 32;                 // queries per iteration
+  static constexpr int KSTEPS = D / (2 * KPL);  // 32x32 MFMA steps over d
+  static constexpr int TSTEPS = 16 / KPL;       // 32x32 MFMA steps over 32 queries
+  static constexpr int NOB = D / 32;            // 32-wide d blocks of dK, dV
+  // Q / dO rows are read two ways: 16 bytes per lane down 16 rows (MFMA A
+  // operand) and 4 rows x 64 bytes per half-wave (transposing read).  No
+  // padding is conflict-free for both, so 16-bit rows are unpadded with
+  // XOR-swizzled 16-byte chunks (Layout); fp32 rows are padded by 16 bytes.
+  static constexpr int PITCH = (E == 4) ? D * E + 16 : D * E;
+  static constexpr int QBYTES = BQ * PITCH;     // one staged Q (or dO) block
+  static constexpr int CPR = D * E / 16;        // 16-byte chunks per row
+  static constexpr int CPTQ = BQ * CPR / (64 * WAVES);  // staged chunks / thread / tensor
+  static_assert(BQ * CPR % (64 * WAVES) == 0, "query block must split evenly");
+};
 
-// ---------------------------------------------------------------------------
-// 2. Main backward kernel.
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   using C = BwdCfg<T, D>;
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = C::KPL, E = C::E;
-  using LQ = Layout<C::PITCH, D * E, E != 4>;    // Q / dO / K tiles
-  using LS = Layout<C::DSP, C::BQ * E, E != 4>;  // dS^T
+  using LQ = Layout<C::PITCH, D * E, E != 4>;
 
-  // stage[buf][0=Q,1=dO][BQ rows]; the K tile aliases it during set-up.
-  __shared__ __attribute__((aligned(16))) char stage[4 * C::QBYTES];
-  __shared__ __attribute__((aligned(16))) char dst_lds[2][C::BKC * C::DSP];  // dS^T [key][q]
-  __shared__ __attribute__((aligned(16))) float lsed[2][2][C::BQ];           // [buf][lse2, D]
+  __shared__ __attribute__((aligned(16))) char stage[4 * C::QBYTES];      // [buf][Q, dO]
+  __shared__ __attribute__((aligned(16))) float lsed[2][2][C::BQ];        // [buf][lse2, D]
   __shared__ uint16_t blist[SPARSE ? kMaxMaskBlocksB : 1];
   __shared__ int nlist_s;
 
@@ -215,7 +117,6 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   T *dV = static_cast<T *>(p.dv) + base;
   const float *LSE = p.lse + (int64_t)bh * N;
   const float *Dl = p.ws_delta + (int64_t)bh * N;
-  float *dQacc = p.ws_dq + (int64_t)bh * N * D;
 
   int kv_len = N;
   if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
@@ -301,18 +202,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     }
   };
 
-  // ---- set-up: K tile through LDS (for the dQ operand); K, V rows of this
-  // wave into registers as S / dP operands.
-  {
-#pragma unroll
-    for (int u = 0; u < C::CPTK; ++u) {
-      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-      const int kk = k0 + row;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (kk < N) v = ldg16(reinterpret_cast<const char *>(K + (int64_t)kk * p.sn) + col * 16);
-      *reinterpret_cast<u32x4 *>(stage + LQ::off(row, col * 16)) = v;
-    }
-  }
+  // ---- K, V rows of this wave as the B operands of S and dP
   frag kf[C::KSTEPS], vf[C::KSTEPS];
   if (key < N) {
     const T *kr = K + (int64_t)key * p.sn + h * (D / 2);
@@ -329,15 +219,6 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
       vf[s] = frag{};
     }
   }
-  __syncthreads();
-  // dQ operand: K[key][d] for this wave's d blocks (d = (wave*DBW + db)*16 + i)
-  frag kq[C::DBW][C::QSTEPS];
-#pragma unroll
-  for (int db = 0; db < C::DBW; ++db)
-#pragma unroll
-    for (int st = 0; st < C::QSTEPS; ++st)
-      kq[db][st] = colfrag16<T, LQ>(stage, st * 4 * KPL, (wave * C::DBW + db) * 16);
-  __syncthreads();  // the staging buffers are reused from here on
 
   // ---- query-block staging: buffer loads -> registers -> LDS (double
   // buffer).  Lane offsets inside a block are loop invariant, the block start
@@ -404,7 +285,6 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     if (has_next) load_q(qblock_start(it + 1));
     const char *ql = stage + buf * 2 * C::QBYTES;
     const char *dl = ql + C::QBYTES;
-    char *dsl = dst_lds[buf];
 
     // Does any (query, key) pair of this block survive the masks for this wave?
     const bool skip = (kw0 >= kv_len) || (CAUSAL && kw0 > q0 + C::BQ - 1);
@@ -447,63 +327,270 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
           dkacc[nb] = M::mma32(regorder_frag<T, LQ>(ql, 0, t, nb * 32), sb, dkacc[nb]);
         }
       }
-      // dS^T -> LDS: row = key (this lane), 4 consecutive queries per group
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qc = 8 * i + 4 * h;
-        char *dst = dsl + LS::off(32 * wave + l32, qc * E);
-        if constexpr (E == 4) {
-          *reinterpret_cast<f32x4 *>(dst) = f32x4{dp[4 * i], dp[4 * i + 1], dp[4 * i + 2], dp[4 * i + 3]};
-        } else {
-          typedef T t4 __attribute__((ext_vector_type(4)));
-          t4 v;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (T)dp[4 * i + j];
-          *reinterpret_cast<t4 *>(dst) = v;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        char *dst = dsl + LS::off(32 * wave + l32, (8 * i + 4 * h) * E);
-        if constexpr (E == 4) {
-          *reinterpret_cast<f32x4 *>(dst) = f32x4{0.f, 0.f, 0.f, 0.f};
-        } else {
-          *reinterpret_cast<u32x2 *>(dst) = u32x2{0u, 0u};
-        }
-      }
     }
     if (has_next) store_q(buf ^ 1, qblock_start(it + 1));
     __syncthreads();
-
-    // dQ[q0 .. q0+31][wave's d slice] += dS K over the workgroup's keys
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      f32x4 acc[C::DBW];
-#pragma unroll
-      for (int db = 0; db < C::DBW; ++db) acc[db] = f32x4{};
-#pragma unroll
-      for (int st = 0; st < C::QSTEPS; ++st) {
-        const frag a = colfrag16<T, LS>(dsl, st * 4 * KPL, qh * 16);
-#pragma unroll
-        for (int db = 0; db < C::DBW; ++db) acc[db] = M::mma16(a, kq[db][st], acc[db]);
-      }
-      const int g = lane >> 4, i = lane & 15;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = q0 + qh * 16 + 4 * g + r;
-        if (qq < N) {
-#pragma unroll
-          for (int db = 0; db < C::DBW; ++db)
-            unsafeAtomicAdd(dQacc + (int64_t)qq * D + (wave * C::DBW + db) * 16 + i, acc[db][r]);
-        }
-      }
-    }
   }
 
   store_dkdv(dkacc, dvacc);
 }
 
+// ---------------------------------------------------------------------------
+// 3. dQ (query-stationary, same tiling as the forward pass).
+template <typename T, int D>
+struct DqCfg {
+  static constexpr int E = sizeof(T);
+  static constexpr int KPL = Mma<T>::KPL;
+  static constexpr int WAVES = 4;
+  static constexpr int BR = 32 * WAVES;           // queries per workgroup
+  static constexpr int BC = (E == 4) ? 32 : 64;   // keys per LDS tile
+  static constexpr int NSB = BC / 32;             // 32-key blocks per tile
+  static constexpr int NOB = D / 32;              // 32-wide blocks of dQ
+  static constexpr int KSTEPS = D / (2 * KPL);    // MFMA steps over d
+  static constexpr int PSTEPS = 16 / KPL;         // MFMA steps over 32 keys
+  // K rows are read 16 bytes per lane (A operand of S^T) and through the
+  // transposing read (A operand of dQ^T): swizzled 16-bit rows as in bwd_main.
+  static constexpr int PITCH = (E == 4) ? D * E + 16 : D * E;
+  static constexpr int KTILE = BC * PITCH;
+  static constexpr int TILE_BYTES = 2 * KTILE;    // one stage: K then V
+  static constexpr int CPR = D * E / 16;
+  static constexpr int CPT = BC * CPR / (64 * WAVES);
+  static_assert(BC * CPR % (64 * WAVES) == 0, "tile must split evenly");
+};
+
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+__global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
+  using C = DqCfg<T, D>;
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int KPL = C::KPL, E = C::E;
+  using LK = Layout<C::PITCH, D * E, E != 4>;
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::TILE_BYTES];
+  __shared__ uint16_t blist[SPARSE ? kMaxMaskBlocksB : 1];
+  __shared__ int nlist_s;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int N = p.N;
+  const int nqt = (N + C::BR - 1) / C::BR;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / nqt;
+  int qt = logical - bh * nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
+  const int b = bh / p.H, hh = bh - b * p.H;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;
+  const T *Q = static_cast<const T *>(p.q) + base;
+  const T *K = static_cast<const T *>(p.k) + base;
+  const T *V = static_cast<const T *>(p.v) + base;
+  const T *dO = static_cast<const T *>(p.dout) + base;
+  T *dQ = static_cast<T *>(p.dq) + base;
+
+  int kv_len = N;
+  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
+  const int q_tile0 = qt * C::BR;
+  const int qw0 = q_tile0 + 32 * wave;
+  const int qi = qw0 + l32;
+  int kv_hi = kv_len;
+  if (CAUSAL) kv_hi = min(kv_hi, q_tile0 + C::BR);
+
+  // ---- key tiles visited (as in the forward pass)
+  int ntiles;
+  int tiles_per_blk = 1;
+  if constexpr (SPARSE) {
+    tiles_per_blk = p.mb / C::BC;
+    const uint8_t *mrow = p.mask + (int64_t)hh * p.mask_hstride + (int64_t)(q_tile0 / p.mb) * p.nblk;
+    if (wave == 0) {
+      int count = 0;
+      for (int j0 = 0; j0 < p.nblk; j0 += 64) {
+        const int j = j0 + lane;
+        const bool set = j < p.nblk && j * p.mb < kv_hi && mrow[j] != 0;
+        const uint64_t bal = __ballot(set);
+        if (set) blist[count + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)j;
+        count += __popcll(bal);
+      }
+      if (lane == 0) nlist_s = count;
+    }
+    __syncthreads();
+    const int nl = nlist_s;
+    if (nl == 0) {
+      ntiles = 0;
+    } else {
+      const int last0 = (int)blist[nl - 1] * p.mb;
+      const int in_last = min(tiles_per_blk, (kv_hi - last0 + C::BC - 1) / C::BC);
+      ntiles = (nl - 1) * tiles_per_blk + in_last;
+    }
+  } else {
+    ntiles = (kv_hi + C::BC - 1) / C::BC;
+  }
+  auto tile_start = [&](int t) -> int {
+    if constexpr (SPARSE) {
+      const int bi = t / tiles_per_blk;
+      return (int)blist[bi] * p.mb + (t - bi * tiles_per_blk) * C::BC;
+    } else {
+      return t * C::BC;
+    }
+  };
+  const int lim = CAUSAL ? min(kv_len, q_tile0 + 1) : kv_len;
+  int n_full;
+  if constexpr (SPARSE) {
+    n_full = 0;
+    for (int bi = 0; bi * tiles_per_blk < ntiles; ++bi) {
+      const int f = min(tiles_per_blk, max(0, (lim - (int)blist[bi] * p.mb) / C::BC));
+      n_full += f;
+      if (f < tiles_per_blk) break;
+    }
+    n_full = min(n_full, ntiles);
+  } else {
+    n_full = min(ntiles, lim / C::BC);
+  }
+
+  // ---- this wave's Q and dO rows (B operands), LSE and D of the lane's query
+  frag qf[C::KSTEPS], gf[C::KSTEPS];
+  float lse2 = INFINITY, dl = 0.f;
+  if (qi < N) {
+    const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
+    const T *grow = dO + (int64_t)qi * p.sn + h * (D / 2);
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      qf[s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
+      gf[s] = *reinterpret_cast<const frag *>(grow + s * KPL);
+    }
+    const float l = p.lse[(int64_t)bh * N + qi];
+    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;  // no visible key: P = 0
+    dl = p.ws_delta[(int64_t)bh * N + qi];
+  } else {
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      qf[s] = frag{};
+      gf[s] = frag{};
+    }
+  }
+
+  // ---- K/V staging (buffer loads -> registers -> LDS, double buffer)
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, kv_bytes);
+  const int row_bytes = (int)(p.sn * E);
+  int voff[C::CPT];
+#pragma unroll
+  for (int u = 0; u < C::CPT; ++u) {
+    const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+    voff[u] = row * row_bytes + col * 16;
+  }
+  u32x4 stk[C::CPT], stv[C::CPT];
+  auto load_tile = [&](int kv0) {
+    const int so = kv0 * row_bytes;
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      stk[u] = buf_load16(krs, voff[u], so);
+      stv[u] = buf_load16(vrs, voff[u], so);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char *kl = smem + buf * C::TILE_BYTES;
+    char *vl = kl + C::KTILE;
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+      *reinterpret_cast<u32x4 *>(kl + LK::off(row, col * 16)) = stk[u];
+      *reinterpret_cast<u32x4 *>(vl + LK::off(row, col * 16)) = stv[u];
+    }
+  };
+
+  f32x16 qacc[C::NOB];
+#pragma unroll
+  for (int nb = 0; nb < C::NOB; ++nb) qacc[nb] = f32x16{};
+  const float c2 = p.scale_log2;
+
+  auto tile = [&](const char *kl, const char *vl, int kv0, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    f32x16 sacc[C::NSB], dpacc[C::NSB];
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      sacc[sb] = f32x16{};
+      dpacc[sb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        const int off = LK::off(sb * 32 + l32, (h * (D / 2) + s * KPL) * E);
+        sacc[sb] = M::mma32(lds_frag<T>(kl, off), qf[s], sacc[sb]);   // S^T = K Q^T
+        dpacc[sb] = M::mma32(lds_frag<T>(vl, off), gf[s], dpacc[sb]);  // dP^T = V dO^T
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(fmaf(sacc[sb][r], c2, -lse2));
+        if constexpr (MASK) {
+          const int kk = kv0 + sb * 32 + reg_row(r, h);
+          if (!(kk < kv_len && (!CAUSAL || kk <= qi))) pv = 0.f;
+        }
+        dpacc[sb][r] = pv * (dpacc[sb][r] - dl);  // dS^T
+      }
+    // dQ^T += K^T dS^T  (rows = d, cols = this lane's query)
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+      for (int t = 0; t < C::PSTEPS; ++t) {
+        const frag sfrag = pack_frag<T>(dpacc[sb], t * KPL);
+#pragma unroll
+        for (int nb = 0; nb < C::NOB; ++nb)
+          qacc[nb] = M::mma32(regorder_frag<T, LK>(kl, sb * 32, t, nb * 32), sfrag, qacc[nb]);
+      }
+  };
+
+  if (ntiles > 0) {
+    load_tile(tile_start(0));
+    store_tile(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  int it = 0;
+  for (; it < n_full; ++it) {
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(tile_start(it + 1));
+    const char *kl = smem + (it & 1) * C::TILE_BYTES;
+    tile(kl, kl + C::KTILE, tile_start(it), std::integral_constant<bool, false>{});
+    if (has_next) store_tile((it + 1) & 1);
+    __syncthreads();
+  }
+  for (; it < ntiles; ++it) {
+    const int kv0 = tile_start(it);
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(tile_start(it + 1));
+    const char *kl = smem + (it & 1) * C::TILE_BYTES;
+    if (!(CAUSAL && kv0 > qw0 + 31))
+      tile(kl, kl + C::KTILE, kv0, std::integral_constant<bool, true>{});
+    if (has_next) store_tile((it + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- dQ = scale * (dS K)
+  if (qi < N) {
+    T *qrow = dQ + (int64_t)qi * p.sn;
+#pragma unroll
+    for (int nb = 0; nb < C::NOB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = nb * 32 + 8 * i + 4 * h;
+        if constexpr (E == 4) {
+          *reinterpret_cast<f32x4 *>(qrow + d0) =
+              f32x4{qacc[nb][4 * i] * p.scale, qacc[nb][4 * i + 1] * p.scale,
+                    qacc[nb][4 * i + 2] * p.scale, qacc[nb][4 * i + 3] * p.scale};
+        } else {
+          typedef T t4 __attribute__((ext_vector_type(4)));
+          t4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = (T)(qacc[nb][4 * i + j] * p.scale);
+          *reinterpret_cast<t4 *>(qrow + d0) = v;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_main_t(const AttnParams &p, hipStream_t s) {
   using C = BwdCfg<T, D>;
@@ -512,6 +599,17 @@ static hipError_t launch_main_t(const AttnParams &p, hipStream_t s) {
   AttnParams a = p;
   void *args[] = {&a};
   return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_main_kernel<T, D, CAUSAL, SPARSE>),
+                         dim3((unsigned)grid), dim3(256), args, 0, s);
+}
+
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+static hipError_t launch_dq_t(const AttnParams &p, hipStream_t s) {
+  using C = DqCfg<T, D>;
+  const int64_t nqt = (p.N + C::BR - 1) / C::BR;
+  const int64_t grid = (int64_t)p.B * p.H * nqt;
+  AttnParams a = p;
+  void *args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel<T, D, CAUSAL, SPARSE>),
                          dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
@@ -534,9 +632,10 @@ static hipError_t launch_bwd_d(const AttnParams &p, bool sparse, unsigned stages
     if (e != hipSuccess) return e;
   }
   if (stages & FA_BWD_DQ) {
-    const int64_t chunks = rows * (D / (16 / (int)sizeof(T)));
-    e = hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel<T, D>),
-                        dim3((unsigned)((chunks + 255) / 256)), dim3(256), args, 0, s);
+    if (sparse)
+      e = p.causal ? launch_dq_t<T, D, true, true>(p, s) : launch_dq_t<T, D, false, true>(p, s);
+    else
+      e = p.causal ? launch_dq_t<T, D, true, false>(p, s) : launch_dq_t<T, D, false, false>(p, s);
   }
   return e;
 }

@@ -161,6 +161,74 @@ __device__ __forceinline__ i16x4 lds_tr4(const char *lds, int byte_off) {
       (__attribute__((address_space(3))) i16x4 *)(lds + byte_off));
 }
 
+// Byte offset of (row, byte-in-row) in an LDS matrix with row pitch PITCH
+// whose 16-byte chunks are permuted within each row by XOR with swz(row).
+// For 16-bit data the permutations are chosen (and checked on gfx950 with the
+// LDS bank-conflict counter) so that the kernels' access patterns hit distinct
+// banks:
+//   ROWB = 128 (8 chunks): swz = 4*((r>>1)&1) + ((r>>2)&3) -- 16 consecutive
+//     rows at one chunk fall in 16 distinct 16-byte slots of 256 bytes, and 4
+//     consecutive rows (aligned to 4) at an aligned 4-chunk group fall in the
+//     4 distinct 64-byte quarters;
+//   ROWB = 256 (16 chunks): swz = 4*(r&3) + ((r>>2)&3), same two properties;
+//   ROWB = 64 (dS^T, 4 chunks): swz = 2*((r>>3)&1) + ((r>>2)&1) -- rows
+//     {0..3, 8..11} (+4) read as aligned 2-chunk pairs fall in 8 distinct
+//     32-byte slots.
+// SWZ = false: plain rows (fp32 data, padded pitch).
+template <int PITCH, int ROWB, bool SWZ>
+struct Layout {
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (!SWZ) return 0;
+    else if constexpr (ROWB == 128) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    else if constexpr (ROWB == 256) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return 2 * ((r >> 3) & 1) + ((r >> 2) & 1);
+  }
+  static __device__ __forceinline__ int off(int row, int byte) {
+    return row * PITCH + (byte ^ (swz(row) << 4));
+  }
+};
+
+// Element e of MFMA step t in register order, from an LDS matrix with rows =
+// contraction index: M[row0 + reg_row(KPL*t + e, h)][col0 + l32].
+template <typename T, typename L>
+__device__ __forceinline__ typename Mma<T>::frag regorder_frag(const char *lds, int row0, int t, int col0) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (Mma<T>::KPL == 1) {
+    const int row = row0 + reg_row(t, lane >> 5);
+    return *reinterpret_cast<const float *>(lds + L::off(row, (col0 + (lane & 31)) * 4));
+  } else {
+    const int g = lane >> 4, s16 = lane & 15;
+    const int r = row0 + 16 * t + 4 * (g >> 1) + (s16 >> 2);
+    const int col = col0 + 16 * (g & 1) + 4 * (s16 & 3);
+    const i16x4 lo = lds_tr4(lds, L::off(r, col * 2));
+    const i16x4 hi = lds_tr4(lds, L::off(r + 8, col * 2));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(typename Mma<T>::frag, v);
+  }
+}
+
+// 16x16 operand in natural order from an LDS matrix whose rows are the
+// contraction index: lane (g = lane/16, i = lane%16) gets
+// M[row0 + KPL*g + e][col0 + i], e < KPL.
+template <typename T, typename L>
+__device__ __forceinline__ typename Mma<T>::frag colfrag16(const char *lds, int row0, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  if constexpr (Mma<T>::KPL == 1) {
+    return *reinterpret_cast<const float *>(lds + L::off(row0 + g, (col0 + (lane & 15)) * 4));
+  } else {
+    const int s16 = lane & 15;
+    const int r = row0 + 8 * g + (s16 >> 2);
+    const int col = col0 + 4 * (s16 & 3);
+    const i16x4 lo = lds_tr4(lds, L::off(r, col * 2));
+    const i16x4 hi = lds_tr4(lds, L::off(r + 4, col * 2));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(typename Mma<T>::frag, v);
+  }
+}
+
 // Cross half-wave exchange: value held by lane l ^ 32.
 __device__ __forceinline__ float xor32(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -21,7 +21,6 @@ struct AttnParams {
   const void *dout;
   void *dq, *dk, *dv;
   float *ws_delta;    // [B*H*N]  rowsum(dO * O)
-  float *ws_dq;       // [B*H*N*d] float32 dQ accumulator (contiguous)
   // problem
   int32_t B, H, N, d;
   int64_t sb, sh, sn;        // element strides of the [B,H,N,d] tensors
@@ -43,10 +42,7 @@ hipError_t launch_fwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream
 hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, unsigned stages,
                       hipStream_t s);
 
-// Workspace layout shared by fa_api.cpp and fa_bwd.hip.
-inline size_t ws_delta_bytes(int64_t rows) { return (size_t)((rows * 4 + 255) / 256 * 256); }
-inline size_t ws_total_bytes(int64_t rows, int64_t d) {
-  return ws_delta_bytes(rows) + (size_t)(rows * d * 4);
-}
+// Backward workspace: one float per query row (D = rowsum(dO * O)).
+inline size_t ws_total_bytes(int64_t rows) { return (size_t)((rows * 4 + 255) / 256 * 256); }
 
 }  // namespace fa

@@ -126,8 +126,9 @@ fa_status_t fa_fwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
                                void *o, float *lse, void *stream);
 
 /* Size in bytes of the device workspace fa_bwd needs for problem p (0 if p is
- * invalid).  It holds one float32 per query row (rowsum(dO * O)) and a float32
- * [B,H,N,d] accumulator for dQ: O(N d) extra memory, never O(N^2). */
+ * invalid).  It holds one float32 per query row, rowsum(dO * O): O(N) extra
+ * memory (summary page, "Complexity analysis": O(N) beyond inputs and
+ * outputs). */
 size_t fa_bwd_workspace_bytes(const fa_problem_t *p);
 
 /* Backward pass: gradients of <dO, O> (summary page, "Key ideas",
@@ -158,10 +159,11 @@ fa_status_t fa_bwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
 
 /* Stages of the backward launch sequence (bit set for fa_bwd_ex). */
 typedef enum fa_bwd_stage {
-  FA_BWD_PRE = 1,    /* D = rowsum(dO * O) into the workspace; zero the dQ
-                        accumulator                                          */
-  FA_BWD_MAIN = 2,   /* recompute S, P per tile; write dK, dV; accumulate dQ */
-  FA_BWD_DQ = 4,     /* dQ = scale * accumulator, converted to the dtype     */
+  FA_BWD_PRE = 1,    /* D = rowsum(dO * O) into the workspace                */
+  FA_BWD_MAIN = 2,   /* key-stationary pass: recompute S, P per tile; write
+                        dK, dV (reads D)                                     */
+  FA_BWD_DQ = 4,     /* query-stationary pass: recompute S, P per tile; write
+                        dQ (reads D; independent of FA_BWD_MAIN)             */
   FA_BWD_ALL = 7
 } fa_bwd_stage_t;
 
@@ -172,8 +174,9 @@ typedef enum fa_bwd_stage {
  * fa_bwd_blocksparse.  `stages` is a nonzero subset of FA_BWD_ALL; the
  * stages it names run in the order PRE, MAIN, DQ.  Calling with PRE, then
  * MAIN, then DQ on one stream, with the same workspace, gives exactly the
- * result of one call with FA_BWD_ALL.  Arguments a stage does not read are
- * still checked. */
+ * result of one call with FA_BWD_ALL; MAIN and DQ may also run concurrently
+ * (on two streams) once PRE has completed.  Arguments a stage does not read
+ * are still checked. */
 fa_status_t fa_bwd_ex(const fa_problem_t *p, const uint8_t *block_mask,
                       int32_t mask_block, int64_t mask_head_stride,
                       const void *q, const void *k, const void *v,
