@@ -278,56 +278,76 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int it = 0; it < nq; ++it) {
+  // One query block: S, dP, P, dS; dV, dK accumulation.
+  auto block = [&](const char *ql, const char *dl, const float (*ld)[C::BQ], int q0, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    // S = Q K^T and dP = dO V^T  (rows = queries in register order, col = key)
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < C::KSTEPS; ++st) {
+      const int off = LQ::off(l32, (h * (D / 2) + st * KPL) * E);
+      s = M::mma32(lds_frag<T>(ql, off), kf[st], s);
+      dp = M::mma32(lds_frag<T>(dl, off), vf[st], dp);
+    }
+    // P = exp2(S*scale*log2e - LSE*log2e); dS = P (dP - D)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&ld[0][8 * i + 4 * h]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&ld[1][8 * i + 4 * h]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * i + j;
+        float pv = fast_exp2(fmaf(s[r], c2, -l4[j]));
+        if constexpr (MASK) {
+          const int qq = q0 + reg_row(r, h);
+          if (!(key < kv_len && (!CAUSAL || key <= qq))) pv = 0.f;
+        }
+        s[r] = pv;
+        dp[r] = pv * (dp[r] - d4[j]);
+      }
+    }
+    // dV^T += dO^T P ; dK^T += Q^T dS   (rows = d, cols = keys)
+#pragma unroll
+    for (int t = 0; t < C::TSTEPS; ++t) {
+      const frag pb = pack_frag<T>(s, t * KPL);
+      const frag sb = pack_frag<T>(dp, t * KPL);
+#pragma unroll
+      for (int nb = 0; nb < C::NOB; ++nb) {
+        dvacc[nb] = M::mma32(regorder_frag<T, LQ>(dl, 0, t, nb * 32), pb, dvacc[nb]);
+        dkacc[nb] = M::mma32(regorder_frag<T, LQ>(ql, 0, t, nb * 32), sb, dkacc[nb]);
+      }
+    }
+  };
+
+  // Blocks some mask touches come first: the causal diagonal (queries before
+  // the end of this key tile), or every block when the key tile crosses the
+  // padding length.
+  int n_masked = 0;
+  if (k0 + C::BKC > kv_len) {
+    n_masked = nq;
+  } else if (CAUSAL) {
+    while (n_masked < nq && qblock_start(n_masked) < k0 + C::BKC) ++n_masked;
+  }
+
+  int it = 0;
+  for (; it < n_masked; ++it) {
     const int buf = it & 1;
     const int q0 = qblock_start(it);
     const bool has_next = it + 1 < nq;
     if (has_next) load_q(qblock_start(it + 1));
     const char *ql = stage + buf * 2 * C::QBYTES;
-    const char *dl = ql + C::QBYTES;
-
-    // Does any (query, key) pair of this block survive the masks for this wave?
-    const bool skip = (kw0 >= kv_len) || (CAUSAL && kw0 > q0 + C::BQ - 1);
-    if (!skip) {
-      // S = Q K^T and dP = dO V^T  (rows = queries in register order, col = key)
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int st = 0; st < C::KSTEPS; ++st) {
-        const int off = LQ::off(l32, (h * (D / 2) + st * KPL) * E);
-        s = M::mma32(lds_frag<T>(ql, off), kf[st], s);
-        dp = M::mma32(lds_frag<T>(dl, off), vf[st], dp);
-      }
-      const bool need_mask = (kw0 + 32 > kv_len) || (CAUSAL && kw0 + 31 > q0);
-      // P = exp2(S*scale*log2e - LSE*log2e); dS = P (dP - D)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lsed[buf][0][8 * i + 4 * h]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&lsed[buf][1][8 * i + 4 * h]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * i + j;
-          float pv = fast_exp2(fmaf(s[r], c2, -l4[j]));
-          if (need_mask) {
-            const int qq = q0 + reg_row(r, h);
-            const bool ok = key < kv_len && (!CAUSAL || key <= qq);
-            if (!ok) pv = 0.f;
-          }
-          s[r] = pv;
-          dp[r] = pv * (dp[r] - d4[j]);
-        }
-      }
-      // dV^T += dO^T P ; dK^T += Q^T dS   (rows = d, cols = keys)
-#pragma unroll
-      for (int t = 0; t < C::TSTEPS; ++t) {
-        const frag pb = pack_frag<T>(s, t * KPL);
-        const frag sb = pack_frag<T>(dp, t * KPL);
-#pragma unroll
-        for (int nb = 0; nb < C::NOB; ++nb) {
-          dvacc[nb] = M::mma32(regorder_frag<T, LQ>(dl, 0, t, nb * 32), pb, dvacc[nb]);
-          dkacc[nb] = M::mma32(regorder_frag<T, LQ>(ql, 0, t, nb * 32), sb, dkacc[nb]);
-        }
-      }
-    }
+    // skip when no (query, key) pair of the block survives for this wave
+    if (!((kw0 >= kv_len) || (CAUSAL && kw0 > q0 + C::BQ - 1)))
+      block(ql, ql + C::QBYTES, lsed[buf], q0, std::integral_constant<bool, true>{});
+    if (has_next) store_q(buf ^ 1, qblock_start(it + 1));
+    __syncthreads();
+  }
+  for (; it < nq; ++it) {
+    const int buf = it & 1;
+    const bool has_next = it + 1 < nq;
+    if (has_next) load_q(qblock_start(it + 1));
+    const char *ql = stage + buf * 2 * C::QBYTES;
+    block(ql, ql + C::QBYTES, lsed[buf], 0, std::integral_constant<bool, false>{});
     if (has_next) store_q(buf ^ 1, qblock_start(it + 1));
     __syncthreads();
   }
