@@ -1,17 +1,18 @@
 """Throughput of exact attention (forward + backward) on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input: fa_fwd, then
-the backward launch sequence (preprocess, main kernel, dQ conversion) through
-fa_bwd_ex, all on torch's current stream.  Prints ONE JSON line on stdout.
+the backward launch sequence (rowsum(dO*O), the dK/dV kernel, the dQ kernel)
+through fa_bwd_ex, all on torch's current stream.  Prints ONE JSON line on stdout.
 
   value      whole-step TFLOP/s, FLOPs counted as 4*B*H*N^2*d for the forward
              (halved when causal) and 2.5x that for the backward, over the
              wall-clock time of the timed steps (inputs resident in HBM).
   roofline   the kernel with the largest average duration: algorithmic FLOPs
-             of one launch (4*d per visible (query, key) pair forward, 10*d
-             backward) over its average duration from HIP events recorded on
-             the launch stream around every timed launch; peak = dense
-             bf16/fp16 MFMA 2516.6 TFLOP/s.  `traffic` comes from the
+             of one launch over its average duration from HIP events recorded
+             on the launch stream around every timed launch; per visible
+             (query, key) pair: forward 4d (S, PV), backward dK/dV kernel 8d
+             (S, dP, dV, dK), backward dQ kernel 6d (S, dP, dQ; S and dP are
+             recomputed there); peak = dense bf16/fp16 MFMA 2516.6 TFLOP/s.  `traffic` comes from the
              committed rocprofv3 counter summary when it was taken on the
              current kernel sources, else null.
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
@@ -229,7 +230,8 @@ def main():
                           None if inputs["block_mask"] is None else inputs["block_mask"].numpy())
     kernels = {
         "fwd_kernel": (fwd_ms, 4.0 * w.d * pairs),
-        "bwd_main_kernel": (main_ms, 10.0 * w.d * pairs),
+        "bwd_main_kernel": (main_ms, 8.0 * w.d * pairs),
+        "bwd_dq_kernel": (dq_ms, 6.0 * w.d * pairs),
     }
     name = max(kernels, key=lambda n: kernels[n][0])
     dur_ms, alg_flops = kernels[name]
