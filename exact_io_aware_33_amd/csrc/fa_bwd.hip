@@ -37,6 +37,7 @@ namespace fa {
 
 constexpr int kMaxMaskBlocksB = 1024;
 
+
 // ---------------------------------------------------------------------------
 // 1. D = rowsum(dO * O).  One thread per row.
 template <typename T, int D>

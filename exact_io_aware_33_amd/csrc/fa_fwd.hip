@@ -19,8 +19,8 @@
 //
 // gfx950 mapping.  Scores are formed transposed, S^T = K Q^T, on 32x32 MFMAs
 // (A = K rows from LDS, B = this wave's Q rows kept in registers for the whole
-// loop), so every lane owns one query (column) and 16 of its keys per 32-key
-// block; its partner lane (l ^ 32) owns the other 16.  The row max therefore
+// loop), so every lane owns one query (column) of each 32-query block and 16
+// of its keys per 32-key block; its partner lane (l ^ 32) owns the other 16.  The row max therefore
 // needs one cross-half exchange, and P^T, converted in registers, is directly
 // the B operand of O^T += V^T P^T.  V^T fragments come from the row-major V
 // tile in LDS through the transposing LDS read (ds_read_b64_tr_b16).
@@ -32,12 +32,19 @@
 
 namespace fa {
 
-template <typename T, int D>
+template <typename T, int D, bool SPARSE>
 struct FwdCfg {
   static constexpr int E = sizeof(T);
   static constexpr int KPL = Mma<T>::KPL;
   static constexpr int WAVES = 4;
-  static constexpr int BR = 32 * WAVES;           // queries per workgroup
+  // 32-query blocks per wavefront.  Two would give each wave two independent
+  // softmax chains and halve the LDS reads per MFMA, but the extra registers
+  // cost occupancy: measured slower on gfx950 (16K dense: 1.24 -> 1.46 ms,
+  // 4K causal: 0.24 -> 0.27 ms), so one.  QB > 1 must stay off for the
+  // block-sparse path, whose tiles may not span two rows of the block mask.
+  static constexpr int QB = 1;
+  static constexpr int QPW = 32 * QB;             // queries per wavefront
+  static constexpr int BR = QPW * WAVES;          // queries per workgroup
   static constexpr int BC = (E == 4) ? 32 : 64;   // keys per LDS tile
   static constexpr int NSB = BC / 32;             // 32-key score blocks per tile
   static constexpr int NOB = D / 32;              // 32-wide blocks of the output
@@ -58,6 +65,7 @@ struct FwdCfg {
 };
 
 constexpr int kMaxMaskBlocks = 1024;
+
 
 // V^T fragment for step t of 32-key block sb and 32-wide output block nb:
 // element e is V[sb*32 + reg_row(KPL*t + e, h)][nb*32 + l32].
@@ -81,7 +89,7 @@ __device__ __forceinline__ typename Mma<T>::frag vt_frag(const char *vl, int sb,
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
-  using C = FwdCfg<T, D>;
+  using C = FwdCfg<T, D, SPARSE>;
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = C::KPL, PITCH = C::PITCH, E = C::E;
@@ -108,8 +116,8 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   int kv_len = N;
   if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
   const int q_tile0 = qt * C::BR;
-  const int qw0 = q_tile0 + 32 * wave;  // first query of this wave
-  const int qi = qw0 + l32;             // this lane's query
+  const int qw0 = q_tile0 + C::QPW * wave;  // first query of this wave
+  // this lane's query in query block qb is qw0 + 32*qb + l32
   int kv_hi = kv_len;                   // keys >= kv_hi are invisible to the whole tile
   if (CAUSAL) kv_hi = min(kv_hi, q_tile0 + C::BR);
 
@@ -154,14 +162,18 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   // ---- this wave's Q rows, held as MFMA B operands for the whole loop.
   // Step s, half h covers d = h*D/2 + s*KPL + e: each lane reads a contiguous
   // half row.
-  frag qf[C::KSTEPS];
-  if (qi < N) {
-    const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
+  frag qf[C::QB][C::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
-  } else {
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int qi = qw0 + 32 * qb + l32;
+    if (qi < N) {
+      const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = frag{};
+      for (int s = 0; s < C::KSTEPS; ++s) qf[qb][s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) qf[qb][s] = frag{};
+    }
   }
 
   // ---- K/V staging: buffer loads (next tile) -> registers -> LDS (double
@@ -197,11 +209,15 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
     }
   };
 
-  float m_run = -INFINITY;  // running max of scale*log2(e)*S, this lane's query
-  float l_run = 0.f;        // running sum over this lane's half of the keys
-  f32x16 oacc[C::NOB];
+  float m_run[C::QB], l_run[C::QB];  // per query block: running max of
+  f32x16 oacc[C::QB][C::NOB];          // scale*log2(e)*S, this lane's half-sum
 #pragma unroll
-  for (int nb = 0; nb < C::NOB; ++nb) oacc[nb] = f32x16{};
+  for (int qb = 0; qb < C::QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < C::NOB; ++nb) oacc[qb][nb] = f32x16{};
+  }
   const float c2 = p.scale_log2;
 
   // Tiles that no mask touches form a prefix of the list (tiles ascend): a key
@@ -221,66 +237,81 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
     n_full = min(ntiles, lim / C::BC);
   }
 
-  // One key tile: scores, (masking), running max / rescale, exp, PV.
+  // One key tile: scores, (masking), running max / rescale, exp, PV, for every
+  // query block of the wave.
   auto tile = [&](const char *kl, const char *vl, int kv0, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
-    // step 1: S^T = K_j Q_i^T
-    f32x16 sacc[C::NSB];
+    // step 1: S^T = K_j Q_i^T (each K fragment feeds every query block)
+    f32x16 sacc[C::QB][C::NSB];
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
-      sacc[sb] = f32x16{};
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) sacc[qb][sb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         const frag a = lds_frag<T>(kl, (sb * 32 + l32) * PITCH + (h * (D / 2) + s * KPL) * E);
-        sacc[sb] = M::mma32(a, qf[s], sacc[sb]);
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) sacc[qb][sb] = M::mma32(a, qf[qb][s], sacc[qb][sb]);
       }
     }
-    float mx = -INFINITY;
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb)
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const int qi = qw0 + 32 * qb + l32;
+      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (MASK) {
-          const int key = kv0 + sb * 32 + reg_row(r, h);
-          if (!(key < kv_len && (!CAUSAL || key <= qi))) sacc[sb][r] = -INFINITY;
+      for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (MASK) {
+            const int key = kv0 + sb * 32 + reg_row(r, h);
+            if (!(key < kv_len && (!CAUSAL || key <= qi))) sacc[qb][sb][r] = -INFINITY;
+          }
+          mx = fmaxf(mx, sacc[qb][sb][r]);
         }
-        mx = fmaxf(mx, sacc[sb][r]);
+      // steps 2-3: running max; the carried state is rescaled only when some
+      // lane's max grew (exp2(0) = 1 for the others)
+      mx = fmaxf(mx, xor32(mx));
+      const float mt = (MASK && mx == -INFINITY) ? -INFINITY : mx * c2;
+      const float m_new = fmaxf(m_run[qb], mt);
+      const float m_use = (MASK && m_new == -INFINITY) ? 0.f : m_new;
+      if (__ballot(m_new > m_run[qb]) != 0) {
+        const float alpha = fast_exp2(m_run[qb] - m_use);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < C::NOB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha;
       }
-    // steps 2-3: running max; the carried state is rescaled only when some
-    // lane's max grew (exp2(0) = 1 for the others)
-    mx = fmaxf(mx, xor32(mx));
-    const float mt = (MASK && mx == -INFINITY) ? -INFINITY : mx * c2;
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (MASK && m_new == -INFINITY) ? 0.f : m_new;
-    if (__ballot(m_new > m_run) != 0) {
-      const float alpha = fast_exp2(m_run - m_use);
-      l_run *= alpha;
+      m_run[qb] = m_new;
 #pragma unroll
-      for (int nb = 0; nb < C::NOB; ++nb)
+      for (int sb = 0; sb < C::NSB; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          float x = fast_exp2(fmaf(sacc[qb][sb][r], c2, -m_use));
+          if constexpr (MASK) {
+            if (sacc[qb][sb][r] == -INFINITY) x = 0.f;
+          }
+          sacc[qb][sb][r] = x;
+        }
     }
-    m_run = m_new;
-#pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = fast_exp2(fmaf(sacc[sb][r], c2, -m_use));
-        if constexpr (MASK) {
-          if (sacc[sb][r] == -INFINITY) x = 0.f;
-        }
-        sacc[sb][r] = x;
-      }
-    // step 4: O_i^T += V_j^T P^T; the row sum takes the same rounded P
+    // step 4: O_i^T += V_j^T P^T; the row sum takes the same rounded P.  Each
+    // V^T fragment feeds every query block.
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb)
 #pragma unroll
       for (int t = 0; t < C::PSTEPS; ++t) {
-        const frag pb = pack_frag<T>(sacc[sb], t * KPL);
-        l_run = frag_sum<T>(pb, l_run);
+        frag pb[C::QB];
 #pragma unroll
-        for (int nb = 0; nb < C::NOB; ++nb)
-          oacc[nb] = M::mma32(vt_frag<T, C::VPITCH>(vl, sb, t, nb), pb, oacc[nb]);
+        for (int qb = 0; qb < C::QB; ++qb) {
+          pb[qb] = pack_frag<T>(sacc[qb][sb], t * KPL);
+          l_run[qb] = frag_sum<T>(pb[qb], l_run[qb]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < C::NOB; ++nb) {
+          const frag va = vt_frag<T, C::VPITCH>(vl, sb, t, nb);
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) oacc[qb][nb] = M::mma32(va, pb[qb], oacc[qb][nb]);
+        }
       }
   };
 
@@ -308,42 +339,46 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
     const bool has_next = it + 1 < ntiles;
     if (has_next) load_tile(tile_start(it + 1));
     const char *kl = smem + (it & 1) * C::TILE_BYTES;
-    if (!(CAUSAL && kv0 > qw0 + 31))  // some key of the tile is visible to this wave
+    if (!(CAUSAL && kv0 > qw0 + C::QPW - 1))  // some key of the tile is visible to this wave
       tile(kl, kl + C::KTILE, kv0, std::integral_constant<bool, true>{});
     if (has_next) store_tile((it + 1) & 1);
     __syncthreads();
   }
 
   // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2
-  const float l_tot = l_run + xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qi < N) {
-    T *orow = O + (int64_t)qi * p.sn;
 #pragma unroll
-    for (int nb = 0; nb < C::NOB; ++nb)
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int qi = qw0 + 32 * qb + l32;
+    const float l_tot = l_run[qb] + xor32(l_run[qb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qi < N) {
+      T *orow = O + (int64_t)qi * p.sn;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = nb * 32 + 8 * i + 4 * h;
-        if constexpr (E == 4) {
-          f32x4 v = {oacc[nb][4 * i] * inv, oacc[nb][4 * i + 1] * inv, oacc[nb][4 * i + 2] * inv,
-                     oacc[nb][4 * i + 3] * inv};
-          *reinterpret_cast<f32x4 *>(orow + d0) = v;
-        } else {
-          typedef T t4 __attribute__((ext_vector_type(4)));
-          t4 v;
+      for (int nb = 0; nb < C::NOB; ++nb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (T)(oacc[nb][4 * i + j] * inv);
-          *reinterpret_cast<t4 *>(orow + d0) = v;
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = nb * 32 + 8 * i + 4 * h;
+          if constexpr (E == 4) {
+            f32x4 v = {oacc[qb][nb][4 * i] * inv, oacc[qb][nb][4 * i + 1] * inv,
+                       oacc[qb][nb][4 * i + 2] * inv, oacc[qb][nb][4 * i + 3] * inv};
+            *reinterpret_cast<f32x4 *>(orow + d0) = v;
+          } else {
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            t4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (T)(oacc[qb][nb][4 * i + j] * inv);
+            *reinterpret_cast<t4 *>(orow + d0) = v;
+          }
         }
-      }
-    if (h == 0)
-      p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      if (h == 0)
+        p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
   }
 }
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_fwd_t(const AttnParams &p, hipStream_t s) {
-  using C = FwdCfg<T, D>;
+  using C = FwdCfg<T, D, SPARSE>;
   const int64_t nqt = (p.N + C::BR - 1) / C::BR;
   const int64_t grid = (int64_t)p.B * p.H * nqt;
   AttnParams a = p;
