@@ -73,7 +73,10 @@ struct BwdCfg {
   static constexpr int KPL = Mma<T>::KPL;
   static constexpr int WAVES = 4;
   static constexpr int BKC = 32 * WAVES;        // keys per workgroup
-  static constexpr int BQ = 32;                 // queries per iteration
+  // queries per iteration: two 32-row sub-blocks for 16-bit types (twice the
+  // MFMA work per barrier and two independent score chains per wave)
+  static constexpr int BQ = (E == 2) ? 64 : 32;
+  static constexpr int QSB = BQ / 32;           // 32-query sub-blocks
   static constexpr int KSTEPS = D / (2 * KPL);  // 32x32 MFMA steps over d
   static constexpr int TSTEPS = 16 / KPL;       // 32x32 MFMA steps over 32 queries
   static constexpr int NOB = D / 32;            // 32-wide d blocks of dK, dV
@@ -282,42 +285,52 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // One query block: S, dP, P, dS; dV, dK accumulation.
   auto block = [&](const char *ql, const char *dl, const float (*ld)[C::BQ], int q0, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
-    // S = Q K^T and dP = dO V^T  (rows = queries in register order, col = key)
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // S = Q K^T and dP = dO V^T per 32-query sub-block (rows = queries in
+    // register order, col = key)
+    f32x16 s[C::QSB], dp[C::QSB];
 #pragma unroll
-    for (int st = 0; st < C::KSTEPS; ++st) {
-      const int off = LQ::off(l32, (h * (D / 2) + st * KPL) * E);
-      s = M::mma32(lds_frag<T>(ql, off), kf[st], s);
-      dp = M::mma32(lds_frag<T>(dl, off), vf[st], dp);
+    for (int qs = 0; qs < C::QSB; ++qs) {
+      s[qs] = f32x16{};
+      dp[qs] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < C::KSTEPS; ++st) {
+        const int off = LQ::off(32 * qs + l32, (h * (D / 2) + st * KPL) * E);
+        s[qs] = M::mma32(lds_frag<T>(ql, off), kf[st], s[qs]);
+        dp[qs] = M::mma32(lds_frag<T>(dl, off), vf[st], dp[qs]);
+      }
     }
     // P = exp2(S*scale*log2e - LSE*log2e); dS = P (dP - D)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&ld[0][8 * i + 4 * h]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&ld[1][8 * i + 4 * h]);
+    for (int qs = 0; qs < C::QSB; ++qs)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * i + j;
-        float pv = fast_exp2(fmaf(s[r], c2, -l4[j]));
-        if constexpr (MASK) {
-          const int qq = q0 + reg_row(r, h);
-          if (!(key < kv_len && (!CAUSAL || key <= qq))) pv = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&ld[0][32 * qs + 8 * i + 4 * h]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&ld[1][32 * qs + 8 * i + 4 * h]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * i + j;
+          float pv = fast_exp2(fmaf(s[qs][r], c2, -l4[j]));
+          if constexpr (MASK) {
+            const int qq = q0 + 32 * qs + reg_row(r, h);
+            if (!(key < kv_len && (!CAUSAL || key <= qq))) pv = 0.f;
+          }
+          s[qs][r] = pv;
+          dp[qs][r] = pv * (dp[qs][r] - d4[j]);
         }
-        s[r] = pv;
-        dp[r] = pv * (dp[r] - d4[j]);
       }
-    }
     // dV^T += dO^T P ; dK^T += Q^T dS   (rows = d, cols = keys)
 #pragma unroll
-    for (int t = 0; t < C::TSTEPS; ++t) {
-      const frag pb = pack_frag<T>(s, t * KPL);
-      const frag sb = pack_frag<T>(dp, t * KPL);
+    for (int qs = 0; qs < C::QSB; ++qs)
 #pragma unroll
-      for (int nb = 0; nb < C::NOB; ++nb) {
-        dvacc[nb] = M::mma32(regorder_frag<T, LQ>(dl, 0, t, nb * 32), pb, dvacc[nb]);
-        dkacc[nb] = M::mma32(regorder_frag<T, LQ>(ql, 0, t, nb * 32), sb, dkacc[nb]);
+      for (int t = 0; t < C::TSTEPS; ++t) {
+        const frag pb = pack_frag<T>(s[qs], t * KPL);
+        const frag sb = pack_frag<T>(dp[qs], t * KPL);
+#pragma unroll
+        for (int nb = 0; nb < C::NOB; ++nb) {
+          dvacc[nb] = M::mma32(regorder_frag<T, LQ>(dl, 32 * qs, t, nb * 32), pb, dvacc[nb]);
+          dkacc[nb] = M::mma32(regorder_frag<T, LQ>(ql, 32 * qs, t, nb * 32), sb, dkacc[nb]);
+        }
       }
-    }
   };
 
   // Blocks some mask touches come first: the causal diagonal (queries before
