@@ -142,6 +142,35 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voffse
                                        r, voffset, __builtin_amdgcn_readfirstlane(soffset), 0));
 }
 
+// Buffer descriptor words (base, stride 0, `bytes` records, raw addressing)
+// for the LDS-DMA load below, which takes the descriptor as SGPR operands.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), (int)bytes, 0x00020000};
+}
+// LDS-DMA: lane i loads 16 bytes at voffset + soffset of the buffer and the
+// hardware writes them to LDS byte address lds_addr + 16 i (gfx950
+// buffer_load_dwordx4 with the lds bit; lds_addr goes in M0 and must be
+// wave-uniform, as must soffset).  Out-of-range lanes deliver zeros.  Written
+// as inline assembly so that the compiler does not make every later LDS read
+// wait for it: the caller waits for the vector-memory counter (and
+// synchronises the workgroup) before reading the destination.  The compiler
+// does not see inside the statement, so it carries its own wait states: an
+// SGPR operand may have just been written by a VALU instruction
+// (v_readfirstlane), which needs 5 before a vector-memory read of it, and M0
+// needs 1 before the LDS-DMA read of it.
+__device__ __forceinline__ void buf_load16_lds(i32x4 rsrc, uint32_t lds_addr, int voffset, int soffset) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "s"(soffset), "{m0}"(lds_addr)
+               : "memory");
+}
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
 // ---- LDS reads ---------------------------------------------------------------
 // KPL contiguous elements of type T at byte offset `off` of LDS.
 template <typename T>

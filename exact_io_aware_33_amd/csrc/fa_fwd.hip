@@ -37,29 +37,28 @@ struct FwdCfg {
   static constexpr int E = sizeof(T);
   static constexpr int KPL = Mma<T>::KPL;
   static constexpr int WAVES = 4;
-  // 32-query blocks per wavefront.  Two would give each wave two independent
-  // softmax chains and halve the LDS reads per MFMA, but the extra registers
-  // cost occupancy: measured slower on gfx950 (16K dense: 1.24 -> 1.46 ms,
-  // 4K causal: 0.24 -> 0.27 ms), so one.  QB > 1 must stay off for the
-  // block-sparse path, whose tiles may not span two rows of the block mask.
-  static constexpr int QB = 1;
-  static constexpr int QPW = 32 * QB;             // queries per wavefront
+  // One 32-query block per wavefront.  Two (each K / V fragment feeding two
+  // query blocks) were measured slower on gfx950: the extra accumulators cost
+  // occupancy.  The block-sparse path also relies on a workgroup's queries
+  // lying in one row of the block mask.
+  static constexpr int QPW = 32;                  // queries per wavefront
   static constexpr int BR = QPW * WAVES;          // queries per workgroup
   static constexpr int BC = (E == 4) ? 32 : 64;   // keys per LDS tile
   static constexpr int NSB = BC / 32;             // 32-key score blocks per tile
   static constexpr int NOB = D / 32;              // 32-wide blocks of the output
   static constexpr int KSTEPS = D / (2 * KPL);    // MFMA steps over d
   static constexpr int PSTEPS = 16 / KPL;         // MFMA steps over 32 keys
-  // LDS row pitches, chosen so that the reads of each tile are free of bank
-  // conflicts (measured on gfx950): K rows are read 16 bytes per lane down 16
-  // consecutive rows (pitch = 16 mod 32 bytes); V rows are read by the
-  // transposing read, 4 rows x 64 bytes per half-wave (pitch = 64 mod 256).
-  static constexpr int PITCH = D * E + 16;        // K tile row pitch (bytes)
-  static constexpr int VPITCH = (E == 4) ? D * E + 16 : D * E + 64;  // V tile row pitch
-  static constexpr int KTILE = BC * PITCH;
-  static constexpr int VTILE = BC * VPITCH;
-  static constexpr int TILE_BYTES = KTILE + VTILE;  // one stage: K then V
-  static constexpr int CPR = D * E / 16;          // 16-byte chunks per row
+  // LDS tiles.  16-bit types: unpadded rows whose 16-byte chunks are permuted
+  // by an XOR swizzle (Layout), filled straight from memory by LDS-DMA buffer
+  // loads; both read patterns (K rows 16 bytes per lane down 16 consecutive
+  // rows; V through the transposing read, 4 rows x 64 bytes per half-wave) are
+  // then free of bank conflicts.  fp32: padded rows filled from registers.
+  static constexpr bool DMA = (E == 2);
+  static constexpr int ROWB = D * E;
+  static constexpr int PITCH = DMA ? ROWB : ROWB + 16;
+  using LT = Layout<PITCH, ROWB, DMA>;
+  static constexpr int TILE = BC * PITCH;         // one K or V tile (bytes)
+  static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
   static constexpr int CPT = BC * CPR / (64 * WAVES);  // chunks per thread
   static_assert(BC * CPR % (64 * WAVES) == 0, "tile must split evenly");
 };
@@ -67,34 +66,31 @@ struct FwdCfg {
 constexpr int kMaxMaskBlocks = 1024;
 
 
-// V^T fragment for step t of 32-key block sb and 32-wide output block nb:
-// element e is V[sb*32 + reg_row(KPL*t + e, h)][nb*32 + l32].
-template <typename T, int PITCH>
-__device__ __forceinline__ typename Mma<T>::frag vt_frag(const char *vl, int sb, int t, int nb) {
-  const int lane = threadIdx.x & 63;
-  if constexpr (Mma<T>::KPL == 1) {
-    const int row = sb * 32 + reg_row(t, lane >> 5);
-    return *reinterpret_cast<const float *>(vl + row * PITCH + (nb * 32 + (lane & 31)) * 4);
-  } else {
-    const int g = lane >> 4, s16 = lane & 15;
-    const int row0 = sb * 32 + 16 * t + 4 * (g >> 1) + (s16 >> 2);
-    const int col = nb * 32 + 16 * (g & 1) + 4 * (s16 & 3);
-    const i16x4 lo = lds_tr4(vl, row0 * PITCH + col * 2);
-    const i16x4 hi = lds_tr4(vl, (row0 + 8) * PITCH + col * 2);
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(typename Mma<T>::frag, v);
-  }
-}
+// Slack of the running max, in log2 units: the stored max is raised only when
+// some lane's tile max exceeds it by more than this, so the exponentials stay
+// below 2^kMaxSlack.  Any reference point gives the same O = (sum p v) / l and
+// LSE = m + log l in exact arithmetic; this one makes the rescale of the
+// partial output rare instead of frequent.
+constexpr float kMaxSlack = 8.0f;
+
+// Scheduling fence: the compiler keeps the instructions on each side of it
+// apart, so the source order of the interleaved MFMA / vector groups below is
+// the issue order.
+#define FA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   using C = FwdCfg<T, D, SPARSE>;
   using M = Mma<T>;
   using frag = typename M::frag;
-  constexpr int KPL = C::KPL, PITCH = C::PITCH, E = C::E;
+  using LT = typename C::LT;
+  constexpr int KPL = C::KPL, E = C::E, NSB = C::NSB;
+  using ffalse = std::integral_constant<bool, false>;
+  using ftrue = std::integral_constant<bool, true>;
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::TILE_BYTES];
+  // Two K slots and two V slots.  Iteration j reads V_{j-1} and K_{j+1} and
+  // fills the other two slots with V_j and K_{j+2}.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
   __shared__ uint16_t blist[SPARSE ? kMaxMaskBlocks : 1];
   __shared__ int nlist_s;
 
@@ -117,8 +113,8 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
   const int q_tile0 = qt * C::BR;
   const int qw0 = q_tile0 + C::QPW * wave;  // first query of this wave
-  // this lane's query in query block qb is qw0 + 32*qb + l32
-  int kv_hi = kv_len;                   // keys >= kv_hi are invisible to the whole tile
+  const int qi = qw0 + l32;                 // this lane's query
+  int kv_hi = kv_len;                       // keys >= kv_hi are invisible to the whole tile
   if (CAUSAL) kv_hi = min(kv_hi, q_tile0 + C::BR);
 
   // ---- the list of key tiles this workgroup visits
@@ -158,66 +154,81 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
       return t * C::BC;
     }
   };
+  // Tile t holds a key visible to some query of this wave.  Tiles ascend, so
+  // under the causal mask the visible tiles are a prefix of the list.
+  auto visible = [&](int t) -> bool { return !CAUSAL || tile_start(t) <= qw0 + C::QPW - 1; };
 
   // ---- this wave's Q rows, held as MFMA B operands for the whole loop.
   // Step s, half h covers d = h*D/2 + s*KPL + e: each lane reads a contiguous
   // half row.
-  frag qf[C::QB][C::KSTEPS];
+  frag qf[C::KSTEPS];
+  if (qi < N) {
+    const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const int qi = qw0 + 32 * qb + l32;
-    if (qi < N) {
-      const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
+    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
+  } else {
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) qf[qb][s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
-    } else {
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) qf[qb][s] = frag{};
-    }
+    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = frag{};
   }
 
-  // ---- K/V staging: buffer loads (next tile) -> registers -> LDS (double
-  // buffer).  Lane offsets inside a tile are loop invariant; the tile start
-  // goes in the scalar offset, and rows past N read as zeros.
+  // ---- K/V tiles into LDS.  Buffer loads with the tile start in the scalar
+  // offset; rows past N read as zeros.  16-bit types: LDS-DMA, each wave
+  // instruction writing 1 KB of the tile (lane i -> byte 16 i) and fetching
+  // the chunk that the swizzle places there.  fp32: through registers.
   const uint32_t kv_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, kv_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, kv_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, kv_bytes), vrs = make_rsrc(V, kv_bytes);
+  const i32x4 kwords = rsrc_words(K, kv_bytes), vwords = rsrc_words(V, kv_bytes);
+  const uint32_t lds0 = lds_addr(smem);
   const int row_bytes = (int)(p.sn * E);
   int voff[C::CPT];
 #pragma unroll
   for (int u = 0; u < C::CPT; ++u) {
-    const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-    voff[u] = row * row_bytes + col * 16;
+    if constexpr (C::DMA) {
+      const int c = 64 * (C::WAVES * u + wave) + lane;  // physical chunk
+      const int row = c / C::CPR, pc = c - row * C::CPR;
+      voff[u] = row * row_bytes + ((pc ^ LT::swz(row)) << 4);
+    } else {
+      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+      voff[u] = row * row_bytes + col * 16;
+    }
   }
-  u32x4 stk[C::CPT], stv[C::CPT];
-  auto load_tile = [&](int kv0) {
-    const int so = kv0 * row_bytes;
+  u32x4 stk[C::DMA ? 1 : C::CPT], stv[C::DMA ? 1 : C::CPT];
+  auto kslot = [&](int t) -> char * { return smem + (t & 1) * C::TILE; };
+  auto vslot = [&](int t) -> char * { return smem + (2 + (t & 1)) * C::TILE; };
+  // fetch: start moving tile `kv0` of `rs` towards LDS slot `dst` (staged in
+  // `st` for fp32); commit: finish (fp32 register stores).  The caller waits
+  // for the memory counter and synchronises before the slot is read.
+  auto fetch = [&](bool is_v, u32x4 *st, char *dst, int kv0) {
+    const int so = __builtin_amdgcn_readfirstlane(kv0 * row_bytes);
 #pragma unroll
     for (int u = 0; u < C::CPT; ++u) {
-      stk[u] = buf_load16(krs, voff[u], so);
-      stv[u] = buf_load16(vrs, voff[u], so);
+      if constexpr (C::DMA) {
+        const uint32_t la = lds0 + (uint32_t)(dst - smem) + 1024 * (C::WAVES * u + wave);
+        buf_load16_lds(is_v ? vwords : kwords, __builtin_amdgcn_readfirstlane(la), voff[u], so);
+      } else {
+        st[u] = buf_load16(is_v ? vrs : krs, voff[u], so);
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-    char *kl = smem + buf * C::TILE_BYTES;
-    char *vl = kl + C::KTILE;
+  auto commit = [&](const u32x4 *st, char *dst) {
+    if constexpr (!C::DMA) {
 #pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-      *reinterpret_cast<u32x4 *>(kl + row * PITCH + col * 16) = stk[u];
-      *reinterpret_cast<u32x4 *>(vl + row * C::VPITCH + col * 16) = stv[u];
+      for (int u = 0; u < C::CPT; ++u) {
+        const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+        *reinterpret_cast<u32x4 *>(dst + row * C::PITCH + col * 16) = st[u];
+      }
     }
   };
 
-  float m_run[C::QB], l_run[C::QB];  // per query block: running max of
-  f32x16 oacc[C::QB][C::NOB];          // scale*log2(e)*S, this lane's half-sum
+  // Carried state (section "Incremental softmax tracking"): m_run is the
+  // reference point of the exponentials (a running max of scale*log2(e)*S,
+  // raised lazily), lpart this lane's share of the exponential sum (four
+  // independent partial sums), oacc the unnormalised output O^T.
+  float m_run = -INFINITY;
+  float lpart[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x16 oacc[C::NOB];
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < C::NOB; ++nb) oacc[qb][nb] = f32x16{};
-  }
+  for (int nb = 0; nb < C::NOB; ++nb) oacc[nb] = f32x16{};
   const float c2 = p.scale_log2;
 
   // Tiles that no mask touches form a prefix of the list (tiles ascend): a key
@@ -237,142 +248,269 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
     n_full = min(ntiles, lim / C::BC);
   }
 
-  // One key tile: scores, (masking), running max / rescale, exp, PV, for every
-  // query block of the wave.
-  auto tile = [&](const char *kl, const char *vl, int kv0, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    // step 1: S^T = K_j Q_i^T (each K fragment feeds every query block)
-    f32x16 sacc[C::QB][C::NSB];
+  // Operand fragments.  K: rows = keys, 16 bytes per lane.  V^T: rows = keys
+  // in register order, through the transposing read.
+  auto kfrag = [&](const char *kl, int i) -> frag {
+    const int s = i / NSB, sb = i - s * NSB;
+    return lds_frag<T>(kl, LT::off(sb * 32 + l32, (h * (D / 2) + s * KPL) * E));
+  };
+  auto vfrag = [&](const char *vl, int k, int nb) -> frag {
+    const int sb = k / C::PSTEPS, t = k - sb * C::PSTEPS;
+    return regorder_frag<T, LT>(vl, sb * 32, t, nb * 32);
+  };
+  constexpr int NS1 = NSB * C::PSTEPS;  // PV steps (C::NOB MFMAs each)
+  constexpr int NS2 = NSB * C::KSTEPS;  // score MFMAs
+  constexpr int NEL = NSB * 16;         // score elements per lane per tile
+
+  // Row sum: the four bf16/f16 pairs of a P fragment go to four independent
+  // partial sums (v_dot2 with ones: the sum of exactly the rounded values the
+  // MFMA consumes).
+  auto rowsum = [&](frag pb) {
+    if constexpr (KPL == 1) {
+      lpart[0] += pb;
+    } else {
+      typedef T t2 __attribute__((ext_vector_type(2)));
+      const t2 one = {(T)1.0f, (T)1.0f};
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) sacc[qb][sb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        const frag a = lds_frag<T>(kl, (sb * 32 + l32) * PITCH + (h * (D / 2) + s * KPL) * E);
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) sacc[qb][sb] = M::mma32(a, qf[qb][s], sacc[qb][sb]);
+      for (int q = 0; q < 4; ++q) {
+        const t2 v = {pb[2 * q], pb[2 * q + 1]};
+        if constexpr (__is_same(T, __bf16))
+          lpart[q] = __builtin_amdgcn_fdot2_f32_bf16(v, one, lpart[q], false);
+        else
+          lpart[q] = __builtin_amdgcn_fdot2(v, one, lpart[q], false);
       }
     }
+  };
+
+  // step 1: S^T = K_j Q_i^T for the tile whose K rows are at kl.  Steps over d
+  // alternate between the 32-key blocks so consecutive MFMAs are independent.
+  auto scores = [&](const char *kl, f32x16 (&sacc)[NSB]) {
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const int qi = qw0 + 32 * qb + l32;
-      float mx = -INFINITY;
+    for (int sb = 0; sb < NSB; ++sb) sacc[sb] = f32x16{};
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb)
+    for (int i = 0; i < NS2; ++i) {
+      const int s = i / NSB, sb = i - s * NSB;
+      sacc[sb] = M::mma32(kfrag(kl, i), qf[s], sacc[sb]);
+      FA_FENCE();  // bounds the operand reads in flight (register pressure)
+    }
+  };
+  // Masking of the tile at kv0 (invisible scores -> -inf).
+  auto apply_mask = [&](f32x16 (&sacc)[NSB], int kv0) {
+    // key kv0 + o is visible iff o < lim_o (one bound per lane)
+    const int lim_o = CAUSAL ? min(kv_len, qi + 1) - kv0 : kv_len - kv0;
+    const int o_h = 4 * h;  // reg_row(r, h) = reg_row(r, 0) + 4 h
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if constexpr (MASK) {
-            const int key = kv0 + sb * 32 + reg_row(r, h);
-            if (!(key < kv_len && (!CAUSAL || key <= qi))) sacc[qb][sb][r] = -INFINITY;
-          }
-          mx = fmaxf(mx, sacc[qb][sb][r]);
-        }
-      // steps 2-3: running max; the carried state is rescaled only when some
-      // lane's max grew (exp2(0) = 1 for the others)
-      mx = fmaxf(mx, xor32(mx));
-      const float mt = (MASK && mx == -INFINITY) ? -INFINITY : mx * c2;
-      const float m_new = fmaxf(m_run[qb], mt);
-      const float m_use = (MASK && m_new == -INFINITY) ? 0.f : m_new;
-      if (__ballot(m_new > m_run[qb]) != 0) {
-        const float alpha = fast_exp2(m_run[qb] - m_use);
-        l_run[qb] *= alpha;
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (!(sb * 32 + reg_row(r, 0) + o_h < lim_o)) sacc[sb][r] = -INFINITY;
+  };
+  // steps 2-3 for the scores in S: the row max over both half-waves (four
+  // independent max chains), scaled by scale*log2(e).  The reference point
+  // moves only when some lane's max passed it by more than the slack; then
+  // the carried state -- O, the partial sums and the exponentials P of the
+  // previous tile, not yet added to O -- is rescaled by exp2(old - new).
+  auto update_max = [&](f32x16 (&S)[NSB], f32x16 (&P)[NSB], auto masked) {
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int e = 0; e < NEL; ++e) mx[e & 3] = fmaxf(mx[e & 3], S[e / 16][e % 16]);
+    float m = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+    m = fmaxf(m, xor32(m));
+    const float mt = (decltype(masked)::value && m == -INFINITY) ? -INFINITY : m * c2;
+    if (__ballot(mt > m_run + kMaxSlack) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      if (m_new != -INFINITY) {
+        const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lpart[q] *= alpha;
 #pragma unroll
         for (int nb = 0; nb < C::NOB; ++nb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+#pragma unroll
+        for (int e = 0; e < NEL; ++e) P[e / 16][e % 16] *= alpha;
+        m_run = m_new;
       }
-      m_run[qb] = m_new;
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = fast_exp2(fmaf(sacc[qb][sb][r], c2, -m_use));
-          if constexpr (MASK) {
-            if (sacc[qb][sb][r] == -INFINITY) x = 0.f;
-          }
-          sacc[qb][sb][r] = x;
-        }
     }
-    // step 4: O_i^T += V_j^T P^T; the row sum takes the same rounded P.  Each
-    // V^T fragment feeds every query block.
+  };
+  // step 4: O_i^T += V_j^T P^T for P in `pacc`, plus the row sums.
+  auto pv = [&](const char *vl, const f32x16 (&pacc)[NSB]) {
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb)
+    for (int k = 0; k < NS1; ++k) {
+      const int sb = k / C::PSTEPS, t = k - sb * C::PSTEPS;
+      const frag pb = pack_frag<T>(pacc[sb], t * KPL);
+      rowsum(pb);
 #pragma unroll
-      for (int t = 0; t < C::PSTEPS; ++t) {
-        frag pb[C::QB];
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) {
-          pb[qb] = pack_frag<T>(sacc[qb][sb], t * KPL);
-          l_run[qb] = frag_sum<T>(pb[qb], l_run[qb]);
-        }
-#pragma unroll
-        for (int nb = 0; nb < C::NOB; ++nb) {
-          const frag va = vt_frag<T, C::VPITCH>(vl, sb, t, nb);
-#pragma unroll
-          for (int qb = 0; qb < C::QB; ++qb) oacc[qb][nb] = M::mma32(va, pb[qb], oacc[qb][nb]);
-        }
-      }
+      for (int nb = 0; nb < C::NOB; ++nb) oacc[nb] = M::mma32(vfrag(vl, k, nb), pb, oacc[nb]);
+      FA_FENCE();  // bounds the operand reads in flight (register pressure)
+    }
   };
 
+  // Every iteration j starts with X = S_j (scores of tile j, whose max is
+  // already folded into m_run) and Y = P_{j-1} (exponentials of tile j-1,
+  // already on the m_run scale) and ends with X = P_j, Y = S_{j+1}.
+  //
+  // Generic iteration: any mask, any visibility.  Straight-line code: a tile
+  // that the wave cannot see is fully masked, so its exponentials are 0 and
+  // its PV adds nothing; past the last tile everything is masked.
+  auto iter_any = [&](int j, auto first, f32x16 (&X)[NSB], f32x16 (&Y)[NSB]) {
+    fetch(true, stv, vslot(j), tile_start(j));
+    fetch(false, stk, kslot(j), tile_start(min(j + 2, ntiles - 1)));
+    if constexpr (!decltype(first)::value) pv(vslot(j - 1), Y);
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int e = 0; e < NEL; ++e) {
+      const float x = fast_exp2(fmaf(X[e / 16][e % 16], c2, -m_use));
+      X[e / 16][e % 16] = X[e / 16][e % 16] == -INFINITY ? 0.f : x;  // masked keys (also for scale 0)
+    }
+    scores(kslot(j + 1), Y);
+    apply_mask(Y, j + 1 < ntiles ? tile_start(j + 1) : kv_len);  // all masked past the end
+    update_max(Y, X, ftrue{});
+    commit(stv, vslot(j));
+    commit(stk, kslot(j));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  // Iteration j for unmasked tiles j and j+1 (both visible) with j >= 1:
+  //  A: PV MFMAs of tile j-1 | fragment packing, row sums, x*c - m of tile j
+  //  B: score MFMAs of tile j+1 | exponentials of tile j
+  //  C: row max of tile j+1 and the (rare) rescale.
+  // Operand reads run one group (V) or two (K) ahead of their MFMA.  `par` is
+  // the parity of j (a compile-time constant in the unrolled loop, so every
+  // LDS address is a loop-invariant register plus an immediate).
+  auto iter_steady = [&](int j, auto par, f32x16 (&X)[NSB], f32x16 (&Y)[NSB]) {
+    constexpr int P = decltype(par)::value;
+    fetch(true, stv, vslot(P), tile_start(j));
+    fetch(false, stk, kslot(P), tile_start(min(j + 2, ntiles - 1)));
+    const char *vl = vslot(P ^ 1), *kl = kslot(P ^ 1);
+    const float m_use = m_run;  // finite: every lane sees a key of tile j
+    // ---- A
+    frag vf[2][C::NOB], pbf[2];
+#pragma unroll
+    for (int nb = 0; nb < C::NOB; ++nb) vf[0][nb] = vfrag(vl, 0, nb);
+    pbf[0] = pack_frag<T>(Y[0], 0);
+    FA_FENCE();
+#pragma unroll
+    for (int k = 0; k < NS1; ++k) {
+      const int cb = k & 1;
+      if (k + 1 < NS1) {
+#pragma unroll
+        for (int nb = 0; nb < C::NOB; ++nb) vf[cb ^ 1][nb] = vfrag(vl, k + 1, nb);
+      }
+#pragma unroll
+      for (int nb = 0; nb < C::NOB; ++nb) oacc[nb] = M::mma32(vf[cb][nb], pbf[cb], oacc[nb]);
+      if (k + 1 < NS1) {
+        const int sb = (k + 1) / C::PSTEPS, t = (k + 1) - sb * C::PSTEPS;
+        pbf[cb ^ 1] = pack_frag<T>(Y[sb], t * KPL);
+      }
+      rowsum(pbf[cb]);
+#pragma unroll
+      for (int e = k * NEL / NS1; e < (k + 1) * NEL / NS1; ++e) X[e / 16][e % 16] = fmaf(X[e / 16][e % 16], c2, -m_use);
+      FA_FENCE();
+    }
+    // ---- B
+    frag kf[3];
+    kf[0] = kfrag(kl, 0);
+    if (NS2 > 1) kf[1] = kfrag(kl, 1);
+    FA_FENCE();
+#pragma unroll
+    for (int i = 0; i < NS2; ++i) {
+      const int s = i / NSB, sb = i - s * NSB;
+      if (i + 2 < NS2) kf[(i + 2) % 3] = kfrag(kl, i + 2);
+      Y[sb] = M::mma32(kf[i % 3], qf[s], s == 0 ? f32x16{} : Y[sb]);
+#pragma unroll
+      for (int e = i * NEL / NS2; e < (i + 1) * NEL / NS2; ++e) X[e / 16][e % 16] = fast_exp2(X[e / 16][e % 16]);
+      FA_FENCE();
+    }
+    // ---- C
+    update_max(Y, X, ffalse{});
+    commit(stv, vslot(P));
+    commit(stk, kslot(P));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  // ---- prologue: K_0, K_1 into LDS, S_0 and its max.
+  // SB holds the current tile's scores and SA the previous tile's
+  // exponentials at the top of every iteration (the two arrays trade roles
+  // inside an iteration; `rotate` swaps them back where needed).
+  f32x16 SA[NSB], SB[NSB];
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) SA[sb] = f32x16{};
+  auto rotate = [&]() {
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      const f32x16 t = SA[sb];
+      SA[sb] = SB[sb];
+      SB[sb] = t;
+    }
+  };
   if (ntiles > 0) {
-    load_tile(tile_start(0));
-    store_tile(0);
+    fetch(false, stk, kslot(0), tile_start(0));
+    fetch(false, stv, kslot(1), tile_start(min(1, ntiles - 1)));
+    commit(stk, kslot(0));
+    commit(stv, kslot(1));
   }
   // Retire every outstanding load (Q fragments included) on all paths into
-  // the loop; otherwise the compiler keeps them "pending" at the loop header
-  // and waits on the next tile's prefetch before the first MFMA of each tile.
+  // the loop; otherwise the compiler keeps them "pending" at the loop header.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (ntiles > 0) {  // tile 0 is visible to every wave
+    scores(kslot(0), SB);
+    apply_mask(SB, tile_start(0));
+    update_max(SB, SA, ftrue{});
+  }
+  __syncthreads();  // K_0's slot is refilled by the first iteration
 
-  int it = 0;
-  for (; it < n_full; ++it) {
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(tile_start(it + 1));
-    const char *kl = smem + (it & 1) * C::TILE_BYTES;
-    tile(kl, kl + C::KTILE, tile_start(it), std::integral_constant<bool, false>{});
-    if (has_next) store_tile((it + 1) & 1);
-    __syncthreads();
+  int j = 0;
+  if (ntiles > 0) {
+    iter_any(j++, ftrue{}, SB, SA);
+    rotate();
   }
-  for (; it < ntiles; ++it) {
-    const int kv0 = tile_start(it);
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(tile_start(it + 1));
-    const char *kl = smem + (it & 1) * C::TILE_BYTES;
-    if (!(CAUSAL && kv0 > qw0 + C::QPW - 1))  // some key of the tile is visible to this wave
-      tile(kl, kl + C::KTILE, kv0, std::integral_constant<bool, true>{});
-    if (has_next) store_tile((it + 1) & 1);
-    __syncthreads();
+  const int j_steady = min(n_full, ntiles) - 1;  // tiles j and j+1 unmasked
+  // Two iterations per trip restore the roles at the loop back edge, so the
+  // steady loop needs no register copies.
+  using odd = std::integral_constant<int, 1>;
+  using even = std::integral_constant<int, 0>;
+  for (; j + 1 < j_steady; j += 2) {
+    iter_steady(j, odd{}, SB, SA);
+    iter_steady(j + 1, even{}, SA, SB);
   }
+  if (j < j_steady) {
+    iter_steady(j++, odd{}, SB, SA);
+    rotate();
+  }
+  for (; j < ntiles; ++j) {
+    iter_any(j, ffalse{}, SB, SA);
+    rotate();
+  }
+  if (ntiles > 0) pv(vslot(ntiles - 1), SA);
+  const float l_run = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
 
   // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qi < N) {
+    T *orow = O + (int64_t)qi * p.sn;
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const int qi = qw0 + 32 * qb + l32;
-    const float l_tot = l_run[qb] + xor32(l_run[qb]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qi < N) {
-      T *orow = O + (int64_t)qi * p.sn;
+    for (int nb = 0; nb < C::NOB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < C::NOB; ++nb)
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = nb * 32 + 8 * i + 4 * h;
+        if constexpr (E == 4) {
+          f32x4 v = {oacc[nb][4 * i] * inv, oacc[nb][4 * i + 1] * inv, oacc[nb][4 * i + 2] * inv,
+                     oacc[nb][4 * i + 3] * inv};
+          *reinterpret_cast<f32x4 *>(orow + d0) = v;
+        } else {
+          typedef T t4 __attribute__((ext_vector_type(4)));
+          t4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d0 = nb * 32 + 8 * i + 4 * h;
-          if constexpr (E == 4) {
-            f32x4 v = {oacc[qb][nb][4 * i] * inv, oacc[qb][nb][4 * i + 1] * inv,
-                       oacc[qb][nb][4 * i + 2] * inv, oacc[qb][nb][4 * i + 3] * inv};
-            *reinterpret_cast<f32x4 *>(orow + d0) = v;
-          } else {
-            typedef T t4 __attribute__((ext_vector_type(4)));
-            t4 v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = (T)(oacc[qb][nb][4 * i + j] * inv);
-            *reinterpret_cast<t4 *>(orow + d0) = v;
-          }
+          for (int jj = 0; jj < 4; ++jj) v[jj] = (T)(oacc[nb][4 * i + jj] * inv);
+          *reinterpret_cast<t4 *>(orow + d0) = v;
         }
-      if (h == 0)
-        p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
-    }
+      }
+    if (h == 0) p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
