@@ -37,9 +37,14 @@ namespace fa {
 
 constexpr int kMaxMaskBlocksB = 1024;
 
+// Scheduling fence: the compiler keeps the instructions on each side of it
+// apart, so the source order of interleaved MFMA / vector groups is the issue
+// order.
+#define FA_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O).  One thread per row.
+// 1. D = rowsum(dO * O) and LSE * log2(e).  One thread per row.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(AttnParams p) {
   const int64_t rows = (int64_t)p.B * p.H * p.N;
@@ -63,6 +68,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(AttnParams p) {
     for (int e = 0; e < EPC; ++e) acc = fmaf((float)ta[e], (float)tb[e], acc);
   }
   p.ws_delta[row] = acc;
+  // the saved statistics in the base-2 domain: P = exp2(S*scale*log2e - lse2);
+  // a row that sees no key (LSE = -inf) gets +inf, so its P is 0
+  const float l = p.lse[row];
+  p.ws_lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
 }
 
 // ---------------------------------------------------------------------------
@@ -73,21 +82,31 @@ struct BwdCfg {
   static constexpr int KPL = Mma<T>::KPL;
   static constexpr int WAVES = 4;
   static constexpr int BKC = 32 * WAVES;        // keys per workgroup
-  // queries per iteration: two 32-row sub-blocks for 16-bit types (twice the
-  // MFMA work per barrier and two independent score chains per wave)
-  static constexpr int BQ = (E == 2) ? 64 : 32;
-  static constexpr int QSB = BQ / 32;           // 32-query sub-blocks
+  static constexpr int BQ = 32;                 // queries per block
   static constexpr int KSTEPS = D / (2 * KPL);  // 32x32 MFMA steps over d
   static constexpr int TSTEPS = 16 / KPL;       // 32x32 MFMA steps over 32 queries
   static constexpr int NOB = D / 32;            // 32-wide d blocks of dK, dV
   // Q / dO rows are read two ways: 16 bytes per lane down 16 rows (MFMA A
   // operand) and 4 rows x 64 bytes per half-wave (transposing read).  No
   // padding is conflict-free for both, so 16-bit rows are unpadded with
-  // XOR-swizzled 16-byte chunks (Layout); fp32 rows are padded by 16 bytes.
-  static constexpr int PITCH = (E == 4) ? D * E + 16 : D * E;
-  static constexpr int QBYTES = BQ * PITCH;     // one staged Q (or dO) block
-  static constexpr int CPR = D * E / 16;        // 16-byte chunks per row
-  static constexpr int CPTQ = BQ * CPR / (64 * WAVES);  // staged chunks / thread / tensor
+  // XOR-swizzled 16-byte chunks (Layout) and arrive by LDS-DMA; fp32 rows are
+  // padded by 16 bytes and staged through registers.
+  static constexpr bool DMA = (E == 2);
+  static constexpr int ROWB = D * E;
+  static constexpr int PITCH = DMA ? ROWB : ROWB + 16;
+  static constexpr int QBYTES = BQ * PITCH;     // one Q (or dO) block
+  // One slot: Q block, dO block, then lse*log2(e) and D of 64 rows (one
+  // 4-byte LDS-DMA; the first 32 belong to the block).
+  static constexpr int LSE_OFF = 2 * QBYTES, D_OFF = LSE_OFF + 256;
+  static constexpr int SLOT = 2 * QBYTES + 512;
+  // Ring of query blocks in LDS: iteration i reads blocks i and i+1 while
+  // blocks i+2 (landed or landing) and i+3 (requested now) are in flight.
+  static constexpr int NSLOT = 4;
+  static constexpr int AHEAD = 3;
+  // vector-memory operations per wave per fetched block (16-bit: all DMA)
+  static constexpr int FETCH_OPS = 2 * (BQ * ROWB / 16 / (64 * WAVES)) + 1;
+  static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+  static constexpr int CPTQ = BQ * CPR / (64 * WAVES);  // chunks per thread per tensor
   static_assert(BQ * CPR % (64 * WAVES) == 0, "query block must split evenly");
 };
 
@@ -97,14 +116,16 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = C::KPL, E = C::E;
-  using LQ = Layout<C::PITCH, D * E, E != 4>;
+  using LQ = Layout<C::PITCH, C::ROWB, C::DMA>;
+  using ffalse = std::integral_constant<bool, false>;
+  using ftrue = std::integral_constant<bool, true>;
 
-  __shared__ __attribute__((aligned(16))) char stage[4 * C::QBYTES];      // [buf][Q, dO]
-  __shared__ __attribute__((aligned(16))) float lsed[2][2][C::BQ];        // [buf][lse2, D]
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSLOT * C::SLOT];
   __shared__ uint16_t blist[SPARSE ? kMaxMaskBlocksB : 1];
   __shared__ int nlist_s;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is made explicitly uniform (it selects scalar operands)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const int N = p.N;
   const int nkt = (N + C::BKC - 1) / C::BKC;
@@ -224,114 +245,251 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     }
   }
 
-  // ---- query-block staging: buffer loads -> registers -> LDS (double
-  // buffer).  Lane offsets inside a block are loop invariant, the block start
-  // goes in the scalar offset, and rows past N read as zeros.
+  // ---- query blocks into the LDS ring (block t -> slot t % NSLOT).  Q, dO:
+  // buffer loads with the block start in the scalar offset, rows past N read
+  // as zeros (16-bit: LDS-DMA, fp32: through registers).  lse*log2(e) and D
+  // from the workspace by 4-byte LDS-DMA (waves 0 and 2 the one, 1 and 3 the
+  // other, so every wave issues the same number of operations).  Rows past N
+  // read zeros there too: with zero Q and dO rows they add nothing to dK, dV.
   const uint32_t q_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, q_bytes);
-  const __amdgpu_buffer_rsrc_t dors = make_rsrc(dO, q_bytes);
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(LSE, (uint32_t)N * 4u);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(Dl, (uint32_t)N * 4u);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, q_bytes), dors = make_rsrc(dO, q_bytes);
+  const i32x4 qwords = rsrc_words(Q, q_bytes), dowords = rsrc_words(dO, q_bytes);
+  const i32x4 statwords = (wave & 1) ? rsrc_words(Dl, (uint32_t)N * 4u)
+                                     : rsrc_words(p.ws_lse2 + (int64_t)bh * N, (uint32_t)N * 4u);
+  const uint32_t lds0 = lds_addr(smem);
   const int row_bytes = (int)(p.sn * E);
   int voff[C::CPTQ];
 #pragma unroll
   for (int u = 0; u < C::CPTQ; ++u) {
-    const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-    voff[u] = row * row_bytes + col * 16;
+    if constexpr (C::DMA) {
+      const int c = 64 * (C::WAVES * u + wave) + lane;  // physical chunk
+      const int row = c / C::CPR, pc = c - row * C::CPR;
+      voff[u] = row * row_bytes + ((pc ^ LQ::swz(row)) << 4);
+    } else {
+      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+      voff[u] = row * row_bytes + col * 16;
+    }
   }
-  u32x4 sq[C::CPTQ], sdo[C::CPTQ];
-  float slse = 0.f, sdel = 0.f;
-  auto load_q = [&](int q0) {
-    const int so = q0 * row_bytes;
-#pragma unroll
-    for (int u = 0; u < C::CPTQ; ++u) {
+  u32x4 sq[C::DMA ? 1 : C::CPTQ], sdo[C::DMA ? 1 : C::CPTQ];
+  auto slot = [&](int t) -> char * { return smem + (t & (C::NSLOT - 1)) * C::SLOT; };
+  // fetch1: part u of query block t (clamped to the list; u = CPTQ is the
+  // statistics); commit: finish the fp32 register staging before the barrier.
+  auto fetch1 = [&](int t, int u) {
+    t = min(t, nq - 1);
+    const int q0 = qblock_start(t);
+    const uint32_t la = lds0 + (uint32_t)(slot(t) - smem);
+    if (u == C::CPTQ) {
+      buf_load4_lds(statwords, __builtin_amdgcn_readfirstlane(la + ((wave & 1) ? C::D_OFF : C::LSE_OFF)),
+                    lane * 4, __builtin_amdgcn_readfirstlane(q0 * 4));
+      return;
+    }
+    const int so = __builtin_amdgcn_readfirstlane(q0 * row_bytes);
+    if constexpr (C::DMA) {
+      const uint32_t lu = la + 1024 * (C::WAVES * u + wave);
+      buf_load16_lds(qwords, __builtin_amdgcn_readfirstlane(lu), voff[u], so);
+      buf_load16_lds(dowords, __builtin_amdgcn_readfirstlane(lu + C::QBYTES), voff[u], so);
+    } else {
       sq[u] = buf_load16(qrs, voff[u], so);
       sdo[u] = buf_load16(dors, voff[u], so);
     }
-    if (tid < C::BQ) {
-      const int so4 = __builtin_amdgcn_readfirstlane(q0 * 4);
-      slse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, tid * 4, so4, 0));
-      sdel = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(drs, tid * 4, so4, 0));
+  };
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int u = 0; u <= C::CPTQ; ++u) fetch1(t, u);
+  };
+  auto commit = [&](int t) {
+    if constexpr (!C::DMA) {
+      char *ql = slot(min(t, nq - 1));
+#pragma unroll
+      for (int u = 0; u < C::CPTQ; ++u) {
+        const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+        *reinterpret_cast<u32x4 *>(ql + LQ::off(row, col * 16)) = sq[u];
+        *reinterpret_cast<u32x4 *>(ql + C::QBYTES + LQ::off(row, col * 16)) = sdo[u];
+      }
     }
   };
-  auto store_q = [&](int buf, int q0) {
-    char *ql = stage + buf * 2 * C::QBYTES;
-    char *dl = ql + C::QBYTES;
-#pragma unroll
-    for (int u = 0; u < C::CPTQ; ++u) {
-      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-      *reinterpret_cast<u32x4 *>(ql + LQ::off(row, col * 16)) = sq[u];
-      *reinterpret_cast<u32x4 *>(dl + LQ::off(row, col * 16)) = sdo[u];
-    }
-    if (tid < C::BQ) {
-      // rows past N, and rows that see no key (LSE = -inf), get P = 0
-      const bool in = q0 + tid < N;
-      lsed[buf][0][tid] = (!in || slse == -INFINITY) ? INFINITY : slse * kLog2e;
-      lsed[buf][1][tid] = in ? sdel : 0.f;
-    }
+  // End of an iteration: the block fetched one iteration ago has landed (the
+  // one requested in this iteration may still be in flight), and every wave
+  // is done with the slot that the next iteration refills.
+  auto sync_ring = [&]() {
+    if constexpr (C::DMA) __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::FETCH_OPS));
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
   const float c2 = p.scale_log2;
-  if (nq > 0) {
-    load_q(qblock_start(0));
-    store_q(0, qblock_start(0));
-  }
-  // Retire every outstanding load (K/V operands included) on all paths into
-  // the loop, so the compiler does not wait on the next block's prefetch
-  // inside the loop.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Operand fragments from a slot.  qfrag(i): step s = i / 2 over d, tensor
+  // i % 2 (0 = Q, 1 = dO): rows = queries, 16 bytes per lane.  tfrag(g):
+  // step t = g / (2 NOB) over queries, output block nb, tensor (0 = dO for
+  // dV, 1 = Q for dK): rows = queries in register order, through the
+  // transposing read.
+  auto qfrag = [&](const char *ql, int i) -> frag {
+    const int s = i >> 1, which = i & 1;
+    return lds_frag<T>(ql + which * C::QBYTES, LQ::off(l32, (h * (D / 2) + s * KPL) * E));
+  };
+  auto tfrag = [&](const char *ql, int g) -> frag {
+    const int t = g / (2 * C::NOB), nb = (g >> 1) % C::NOB, which = g & 1;
+    return regorder_frag<T, LQ>(ql + (which ? 0 : C::QBYTES), 0, t, nb * 32);
+  };
+  constexpr int NGA = 2 * C::KSTEPS;            // S / dP MFMAs per block
+  constexpr int NGB = 2 * C::TSTEPS * C::NOB;   // dV / dK MFMAs per block
 
-  // One query block: S, dP, P, dS; dV, dK accumulation.
-  auto block = [&](const char *ql, const char *dl, const float (*ld)[C::BQ], int q0, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    // S = Q K^T and dP = dO V^T per 32-query sub-block (rows = queries in
-    // register order, col = key)
-    f32x16 s[C::QSB], dp[C::QSB];
+  // S = Q K^T, dP = dO V^T for the block in `ql` (rows = queries in register
+  // order, column = this lane's key).
+  auto sdp = [&](const char *ql, f32x16 &S, f32x16 &DP) {
+    S = f32x16{};
+    DP = f32x16{};
 #pragma unroll
-    for (int qs = 0; qs < C::QSB; ++qs) {
-      s[qs] = f32x16{};
-      dp[qs] = f32x16{};
+    for (int i = 0; i < NGA; ++i) {
+      const int s = i >> 1;
+      if (i & 1) DP = M::mma32(qfrag(ql, i), vf[s], DP);
+      else S = M::mma32(qfrag(ql, i), kf[s], S);
+      FA_FENCE();  // bounds the operand reads in flight (register pressure)
+    }
+  };
+  // P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - D), in place; with
+  // MASK, invisible (query, key) pairs get P = dS = 0.
+  auto softmax_grad = [&](const char *ql, int q0, f32x16 &S, f32x16 &DP, auto masked) {
+    const float *ll = reinterpret_cast<const float *>(ql + C::LSE_OFF);
+    const float *dd = reinterpret_cast<const float *>(ql + C::D_OFF);
+    const int lim_q = CAUSAL ? key - q0 : -1;  // query row qr visible iff qr >= lim_q
 #pragma unroll
-      for (int st = 0; st < C::KSTEPS; ++st) {
-        const int off = LQ::off(32 * qs + l32, (h * (D / 2) + st * KPL) * E);
-        s[qs] = M::mma32(lds_frag<T>(ql, off), kf[st], s[qs]);
-        dp[qs] = M::mma32(lds_frag<T>(dl, off), vf[st], dp[qs]);
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ll + 8 * i + 4 * h);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dd + 8 * i + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * i + j;
+        float pv = fast_exp2(fmaf(S[r], c2, -l4[j]));
+        if constexpr (decltype(masked)::value) {
+          if (!(key < kv_len && reg_row(r, h) >= lim_q)) pv = 0.f;
+        }
+        S[r] = pv;
+        DP[r] = pv * (DP[r] - d4[j]);
       }
     }
-    // P = exp2(S*scale*log2e - LSE*log2e); dS = P (dP - D)
-#pragma unroll
-    for (int qs = 0; qs < C::QSB; ++qs)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&ld[0][32 * qs + 8 * i + 4 * h]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&ld[1][32 * qs + 8 * i + 4 * h]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * i + j;
-          float pv = fast_exp2(fmaf(s[qs][r], c2, -l4[j]));
-          if constexpr (MASK) {
-            const int qq = q0 + 32 * qs + reg_row(r, h);
-            if (!(key < kv_len && (!CAUSAL || key <= qq))) pv = 0.f;
-          }
-          s[qs][r] = pv;
-          dp[qs][r] = pv * (dp[qs][r] - d4[j]);
-        }
-      }
-    // dV^T += dO^T P ; dK^T += Q^T dS   (rows = d, cols = keys)
-#pragma unroll
-    for (int qs = 0; qs < C::QSB; ++qs)
-#pragma unroll
-      for (int t = 0; t < C::TSTEPS; ++t) {
-        const frag pb = pack_frag<T>(s[qs], t * KPL);
-        const frag sb = pack_frag<T>(dp[qs], t * KPL);
-#pragma unroll
-        for (int nb = 0; nb < C::NOB; ++nb) {
-          dvacc[nb] = M::mma32(regorder_frag<T, LQ>(dl, 32 * qs, t, nb * 32), pb, dvacc[nb]);
-          dkacc[nb] = M::mma32(regorder_frag<T, LQ>(ql, 32 * qs, t, nb * 32), sb, dkacc[nb]);
-        }
-      }
   };
+  // dV^T += dO^T P, dK^T += Q^T dS (rows = d, column = this lane's key).
+  auto dvdk = [&](const char *ql, const f32x16 &P, const f32x16 &DS) {
+#pragma unroll
+    for (int t = 0; t < C::TSTEPS; ++t) {
+      const frag pb = pack_frag<T>(P, t * KPL);
+      const frag sb = pack_frag<T>(DS, t * KPL);
+#pragma unroll
+      for (int nb = 0; nb < C::NOB; ++nb) {
+        const int g = 2 * (t * C::NOB + nb);
+        dvacc[nb] = M::mma32(tfrag(ql, g), pb, dvacc[nb]);
+        dkacc[nb] = M::mma32(tfrag(ql, g + 1), sb, dkacc[nb]);
+        FA_FENCE();  // bounds the operand reads in flight (register pressure)
+      }
+    }
+  };
+
+  // Every iteration i starts with (SX, DX) = (S_i, dP_i) and ends with
+  // (SX, DX) = (P_i, dS_i) consumed and (SY, DY) = (S_{i+1}, dP_{i+1}).
+  //
+  // Generic iteration: any mask.  Straight-line code; past the last block the
+  // next-block products are computed on a repeated block and never used.
+  auto iter_any = [&](int i, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
+    fetch(i + C::AHEAD);
+    const char *ql = slot(i), *qn = slot(i + 1);
+    softmax_grad(ql, qblock_start(i), SX, DX, ftrue{});
+    sdp(qn, SY, DY);
+    dvdk(ql, SX, DX);
+    commit(i + C::AHEAD);
+    sync_ring();
+  };
+  // Iteration i for an unmasked block i with a successor, as one sequence of
+  // MFMA groups (NGA score / dP MFMAs of block i+1, then NGB dV / dK MFMAs of
+  // block i), each paired with a slice of the vector work of block i:
+  //  during the score MFMAs: P, dS of the first 8 rows (register order), then
+  //    the packing of step 0;
+  //  during the first half of the dV / dK MFMAs: P, dS of the last 8 rows,
+  //    and the packing of step t+1 at the end of step t.
+  // Operand reads run two groups ahead of their MFMA; the next block's
+  // LDS-DMA is spread over the first groups.  `par` is i mod NSLOT (a
+  // compile-time constant in the unrolled loop, so every LDS address is a
+  // loop-invariant register plus an immediate).
+  auto iter_steady = [&](int i, auto par, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
+    constexpr int P = decltype(par)::value;
+    char *const ql = smem + P * C::SLOT;
+    char *const qn = smem + ((P + 1) % C::NSLOT) * C::SLOT;
+    const float *ll = reinterpret_cast<const float *>(ql + C::LSE_OFF);
+    const float *dd = reinterpret_cast<const float *>(ql + C::D_OFF);
+    f32x4 l4[2], d4[2];
+    // P, dS of row r (quad q = r / 4 prefetched one quad ahead)
+    auto row = [&](int r) {
+      const int q = r >> 2, j = r & 3;
+      if (j == 0 && q + 1 < 4) {
+        l4[(q + 1) & 1] = *reinterpret_cast<const f32x4 *>(ll + 8 * (q + 1) + 4 * h);
+        d4[(q + 1) & 1] = *reinterpret_cast<const f32x4 *>(dd + 8 * (q + 1) + 4 * h);
+      }
+      const float pv = fast_exp2(fmaf(SX[r], c2, -l4[q & 1][j]));
+      SX[r] = pv;
+      DX[r] = pv * (DX[r] - d4[q & 1][j]);
+    };
+    // ---- score / dP MFMAs of block i+1
+    frag af[3];
+    af[0] = qfrag(qn, 0);
+    af[1] = qfrag(qn, 1);
+    l4[0] = *reinterpret_cast<const f32x4 *>(ll + 4 * h);
+    d4[0] = *reinterpret_cast<const f32x4 *>(dd + 4 * h);
+    SY = f32x16{};
+    DY = f32x16{};
+    FA_FENCE();
+#pragma unroll
+    for (int g = 0; g < NGA; ++g) {
+      const int s = g >> 1;
+      if (g + 2 < NGA) af[(g + 2) % 3] = qfrag(qn, g + 2);
+      if (g & 1) DY = M::mma32(af[g % 3], vf[s], DY);
+      else SY = M::mma32(af[g % 3], kf[s], SY);
+      if (g <= C::CPTQ) fetch1(i + C::AHEAD, g);
+#pragma unroll
+      for (int r = 8 * g / NGA; r < 8 * (g + 1) / NGA; ++r) row(r);
+      FA_FENCE();
+    }
+    // ---- dV / dK MFMAs of block i
+    frag tf[3], pb[2], sbf[2];
+    tf[0] = tfrag(ql, 0);
+    tf[1] = tfrag(ql, 1);
+    pb[0] = pack_frag<T>(SX, 0);
+    sbf[0] = pack_frag<T>(DX, 0);
+    FA_FENCE();
+#pragma unroll
+    for (int g = 0; g < NGB; ++g) {
+      const int t = g / (2 * C::NOB), nb = (g >> 1) % C::NOB;
+      if (g + 2 < NGB) tf[(g + 2) % 3] = tfrag(ql, g + 2);
+      if (g & 1) dkacc[nb] = M::mma32(tf[g % 3], sbf[t & 1], dkacc[nb]);
+      else dvacc[nb] = M::mma32(tf[g % 3], pb[t & 1], dvacc[nb]);
+      if (g < NGB / 2) {
+#pragma unroll
+        for (int r = 8 + 8 * g / (NGB / 2); r < 8 + 8 * (g + 1) / (NGB / 2); ++r) row(r);
+      }
+      if (g % (2 * C::NOB) == 2 * C::NOB - 1 && t + 1 < C::TSTEPS) {
+        // the next step's operands, once its rows are done
+        pb[(t + 1) & 1] = pack_frag<T>(SX, (t + 1) * KPL);
+        sbf[(t + 1) & 1] = pack_frag<T>(DX, (t + 1) * KPL);
+      }
+      FA_FENCE();
+    }
+    commit(i + C::AHEAD);
+    sync_ring();
+  };
+
+  // ---- prologue: the first AHEAD blocks into the ring, S_0 and dP_0.
+  f32x16 SA, DA, SB, DB;
+  if (nq > 0) {
+#pragma unroll
+    for (int t = 0; t < C::AHEAD; ++t) {
+      fetch(t);
+      commit(t);
+    }
+  }
+  // Retire every outstanding load (K/V operands included) on all paths into
+  // the loop, so the compiler does not wait on a later prefetch inside it.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (nq > 0) sdp(slot(0), SA, DA);
 
   // Blocks some mask touches come first: the causal diagonal (queries before
   // the end of this key tile), or every block when the key tile crosses the
@@ -342,28 +500,38 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   } else if (CAUSAL) {
     while (n_masked < nq && qblock_start(n_masked) < k0 + C::BKC) ++n_masked;
   }
-
-  int it = 0;
-  for (; it < n_masked; ++it) {
-    const int buf = it & 1;
-    const int q0 = qblock_start(it);
-    const bool has_next = it + 1 < nq;
-    if (has_next) load_q(qblock_start(it + 1));
-    const char *ql = stage + buf * 2 * C::QBYTES;
-    // skip when no (query, key) pair of the block survives for this wave
-    if (!((kw0 >= kv_len) || (CAUSAL && kw0 > q0 + C::BQ - 1)))
-      block(ql, ql + C::QBYTES, lsed[buf], q0, std::integral_constant<bool, true>{});
-    if (has_next) store_q(buf ^ 1, qblock_start(it + 1));
-    __syncthreads();
+  // (SA, DA) holds the current block's products at the top of every trip.
+  auto swap_ab = [&]() {
+    const f32x16 ts = SA, td = DA;
+    SA = SB;
+    DA = DB;
+    SB = ts;
+    DB = td;
+  };
+  int i = 0;
+  for (; i < n_masked && i < nq; ++i) {
+    iter_any(i, SA, DA, SB, DB);
+    swap_ab();
   }
-  for (; it < nq; ++it) {
-    const int buf = it & 1;
-    const bool has_next = it + 1 < nq;
-    if (has_next) load_q(qblock_start(it + 1));
-    const char *ql = stage + buf * 2 * C::QBYTES;
-    block(ql, ql + C::QBYTES, lsed[buf], 0, std::integral_constant<bool, false>{});
-    if (has_next) store_q(buf ^ 1, qblock_start(it + 1));
-    __syncthreads();
+  // Steady blocks in trips of NSLOT (so the slots are compile-time
+  // constants); the trip must start at a block index that is 0 mod NSLOT.
+  for (; i < nq - 1 && (i & (C::NSLOT - 1)) != 0; ++i) {
+    iter_any(i, SA, DA, SB, DB);
+    swap_ab();
+  }
+  using s0 = std::integral_constant<int, 0>;
+  using s1 = std::integral_constant<int, 1>;
+  using s2 = std::integral_constant<int, 2>;
+  using s3 = std::integral_constant<int, 3>;
+  for (; i + C::NSLOT < nq; i += C::NSLOT) {
+    iter_steady(i, s0{}, SA, DA, SB, DB);
+    iter_steady(i + 1, s1{}, SB, DB, SA, DA);
+    iter_steady(i + 2, s2{}, SA, DA, SB, DB);
+    iter_steady(i + 3, s3{}, SB, DB, SA, DA);
+  }
+  for (; i < nq; ++i) {
+    iter_any(i, SA, DA, SB, DB);
+    swap_ab();
   }
 
   store_dkdv(dkacc, dvacc);
@@ -490,8 +658,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
       qf[s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
       gf[s] = *reinterpret_cast<const frag *>(grow + s * KPL);
     }
-    const float l = p.lse[(int64_t)bh * N + qi];
-    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;  // no visible key: P = 0
+    lse2 = p.ws_lse2[(int64_t)bh * N + qi];  // +inf when no key is visible: P = 0
     dl = p.ws_delta[(int64_t)bh * N + qi];
   } else {
 #pragma unroll

@@ -166,6 +166,17 @@ __device__ __forceinline__ void buf_load16_lds(i32x4 rsrc, uint32_t lds_addr, in
                : "v"(voffset), "s"(rsrc), "s"(soffset), "{m0}"(lds_addr)
                : "memory");
 }
+// The same with 4 bytes per lane (lane i -> lds_addr + 4 i).
+__device__ __forceinline__ void buf_load4_lds(i32x4 rsrc, uint32_t lds_addr, int voffset, int soffset) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "s"(soffset), "{m0}"(lds_addr)
+               : "memory");
+}
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// the wave are outstanding (other counters not waited on).
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 // 32-bit LDS address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;

@@ -1,14 +1,15 @@
 // Forward pass of exact attention on gfx950: one workgroup per (batch, head,
-// 128-query tile), one wavefront per 32 queries, K/V streamed through LDS in
-// tiles of BC keys with a running row max / row sum.
+// 128-query tile), K/V streamed through LDS in tiles of BC keys with a running
+// row max / row sum.
 //
 // Method (FlashAttention summary page, paper 2205.14135):
 //  * section "Incremental softmax tracking", steps 1-4 for query block i and
 //    key/value block j: block scores, block max / exp / sum, running max/sum
 //    update, rescaled output accumulation.  Here the division by the running
 //    sum is deferred to the epilogue (identical in exact arithmetic) and the
-//    exponentials are taken directly against the running max (the block-local
-//    exp(S - m_block) times exp(m_block - m_new) of the page, folded).
+//    exponentials are taken directly against a running reference point (the
+//    block-local exp(S - m_block) times exp(m_block - m_new) of the page,
+//    folded; see kMaxSlack for how the reference point moves).
 //  * section "Key ideas", tiling bullet: Q, K, V are cut into blocks that fit
 //    on chip; the N x N matrices never reach device memory.
 //  * Math-properties page, section 7: the loop keeps one query tile resident
@@ -18,13 +19,23 @@
 //    set are visited.
 //
 // gfx950 mapping.  Scores are formed transposed, S^T = K Q^T, on 32x32 MFMAs
-// (A = K rows from LDS, B = this wave's Q rows kept in registers for the whole
+// (A = K rows from LDS, B = the wave's Q rows kept in registers for the whole
 // loop), so every lane owns one query (column) of each 32-query block and 16
-// of its keys per 32-key block; its partner lane (l ^ 32) owns the other 16.  The row max therefore
-// needs one cross-half exchange, and P^T, converted in registers, is directly
-// the B operand of O^T += V^T P^T.  V^T fragments come from the row-major V
-// tile in LDS through the transposing LDS read (ds_read_b64_tr_b16).
-// Exponentials are base 2 with scale*log2(e) folded into one FMA.
+// of its keys per 32-key block; its partner lane (l ^ 32) owns the other 16.
+// The row max therefore needs one cross-half exchange, and P^T, converted in
+// registers, is directly the B operand of O^T += V^T P^T.  V^T fragments come
+// from the row-major V tile in LDS through the transposing LDS read
+// (ds_read_b64_tr_b16).  Exponentials are base 2 with scale*log2(e) folded
+// into one FMA.  A wave owns QB 32-query blocks: every K / V fragment read
+// from LDS feeds QB MFMAs, which is what keeps LDS bandwidth below the
+// matrix-core rate for d = 64.
+//
+// Schedule.  K and V tiles move from memory into XOR-swizzled LDS slots by
+// LDS-DMA.  Iteration j overlaps (A) the PV MFMAs of tile j-1 with the
+// packing / row sums of P_{j-1} and the x*c - m of tile j, then (B) the score
+// MFMAs of tile j+1 with the exponentials of tile j, then (C) takes the row
+// max of tile j+1.  The MFMA / vector groups are fenced so that the source
+// order is the issue order.
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -36,15 +47,18 @@ template <typename T, int D, bool SPARSE>
 struct FwdCfg {
   static constexpr int E = sizeof(T);
   static constexpr int KPL = Mma<T>::KPL;
-  static constexpr int WAVES = 4;
-  // One 32-query block per wavefront.  Two (each K / V fragment feeding two
-  // query blocks) were measured slower on gfx950: the extra accumulators cost
-  // occupancy.  The block-sparse path also relies on a workgroup's queries
-  // lying in one row of the block mask.
-  static constexpr int QPW = 32;                  // queries per wavefront
-  static constexpr int BR = QPW * WAVES;          // queries per workgroup
-  static constexpr int BC = (E == 4) ? 32 : 64;   // keys per LDS tile
+  // 32-query blocks per wavefront: two for 16-bit d = 64 (each K / V
+  // fragment feeds two MFMAs, halving LDS reads per MFMA), one otherwise
+  // (d = 128 needs the registers for its output accumulators).
+  static constexpr int QB = (E == 2 && D == 64) ? 2 : 1;
+  static constexpr int WAVES = 4 / QB;
+  static constexpr int NTHR = 64 * WAVES;
+  static constexpr int QPW = 32 * QB;             // queries per wavefront
+  static constexpr int BR = QPW * WAVES;          // queries per workgroup (128)
+  static constexpr int BC = (E == 4 || QB == 2) ? 32 : 64;  // keys per LDS tile
   static constexpr int NSB = BC / 32;             // 32-key score blocks per tile
+  static constexpr int NBLK = QB * NSB;           // 32x32 score blocks per wave
+  static constexpr int NEL = NBLK * 16;           // score elements per lane
   static constexpr int NOB = D / 32;              // 32-wide blocks of the output
   static constexpr int KSTEPS = D / (2 * KPL);    // MFMA steps over d
   static constexpr int PSTEPS = 16 / KPL;         // MFMA steps over 32 keys
@@ -59,18 +73,18 @@ struct FwdCfg {
   using LT = Layout<PITCH, ROWB, DMA>;
   static constexpr int TILE = BC * PITCH;         // one K or V tile (bytes)
   static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
-  static constexpr int CPT = BC * CPR / (64 * WAVES);  // chunks per thread
-  static_assert(BC * CPR % (64 * WAVES) == 0, "tile must split evenly");
+  static constexpr int CPT = BC * CPR / NTHR;     // chunks per thread
+  static_assert(BC * CPR % NTHR == 0, "tile must split evenly");
+  static_assert(BR == 128, "the block-sparse path needs 128-query workgroups");
 };
 
 constexpr int kMaxMaskBlocks = 1024;
 
-
-// Slack of the running max, in log2 units: the stored max is raised only when
-// some lane's tile max exceeds it by more than this, so the exponentials stay
-// below 2^kMaxSlack.  Any reference point gives the same O = (sum p v) / l and
-// LSE = m + log l in exact arithmetic; this one makes the rescale of the
-// partial output rare instead of frequent.
+// Slack of the running reference point, in log2 units: the stored max is
+// raised only when some lane's tile max exceeds it by more than this, so the
+// exponentials stay below 2^kMaxSlack.  Any reference point gives the same
+// O = (sum p v) / l and LSE = m + log l in exact arithmetic; this one makes
+// the rescale of the carried state rare instead of frequent.
 constexpr float kMaxSlack = 8.0f;
 
 // Scheduling fence: the compiler keeps the instructions on each side of it
@@ -79,12 +93,12 @@ constexpr float kMaxSlack = 8.0f;
 #define FA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
+__global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR)) fwd_kernel(AttnParams p) {
   using C = FwdCfg<T, D, SPARSE>;
   using M = Mma<T>;
   using frag = typename M::frag;
   using LT = typename C::LT;
-  constexpr int KPL = C::KPL, E = C::E, NSB = C::NSB;
+  constexpr int KPL = C::KPL, E = C::E, QB = C::QB, NSB = C::NSB, NBLK = C::NBLK, NEL = C::NEL;
   using ffalse = std::integral_constant<bool, false>;
   using ftrue = std::integral_constant<bool, true>;
 
@@ -113,7 +127,7 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
   const int q_tile0 = qt * C::BR;
   const int qw0 = q_tile0 + C::QPW * wave;  // first query of this wave
-  const int qi = qw0 + l32;                 // this lane's query
+  // this lane's query in query block qb is qw0 + 32*qb + l32
   int kv_hi = kv_len;                       // keys >= kv_hi are invisible to the whole tile
   if (CAUSAL) kv_hi = min(kv_hi, q_tile0 + C::BR);
 
@@ -154,21 +168,22 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
       return t * C::BC;
     }
   };
-  // Tile t holds a key visible to some query of this wave.  Tiles ascend, so
-  // under the causal mask the visible tiles are a prefix of the list.
-  auto visible = [&](int t) -> bool { return !CAUSAL || tile_start(t) <= qw0 + C::QPW - 1; };
 
   // ---- this wave's Q rows, held as MFMA B operands for the whole loop.
   // Step s, half h covers d = h*D/2 + s*KPL + e: each lane reads a contiguous
   // half row.
-  frag qf[C::KSTEPS];
-  if (qi < N) {
-    const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
+  frag qf[QB][C::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
-  } else {
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qw0 + 32 * qb + l32;
+    if (qi < N) {
+      const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = frag{};
+      for (int s = 0; s < C::KSTEPS; ++s) qf[qb][s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) qf[qb][s] = frag{};
+    }
   }
 
   // ---- K/V tiles into LDS.  Buffer loads with the tile start in the scalar
@@ -188,47 +203,55 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
       const int row = c / C::CPR, pc = c - row * C::CPR;
       voff[u] = row * row_bytes + ((pc ^ LT::swz(row)) << 4);
     } else {
-      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+      const int c = tid + C::NTHR * u, row = c / C::CPR, col = c - row * C::CPR;
       voff[u] = row * row_bytes + col * 16;
     }
   }
   u32x4 stk[C::DMA ? 1 : C::CPT], stv[C::DMA ? 1 : C::CPT];
   auto kslot = [&](int t) -> char * { return smem + (t & 1) * C::TILE; };
   auto vslot = [&](int t) -> char * { return smem + (2 + (t & 1)) * C::TILE; };
-  // fetch: start moving tile `kv0` of `rs` towards LDS slot `dst` (staged in
-  // `st` for fp32); commit: finish (fp32 register stores).  The caller waits
-  // for the memory counter and synchronises before the slot is read.
-  auto fetch = [&](bool is_v, u32x4 *st, char *dst, int kv0) {
+  // fetch1: start moving part u of tile `kv0` towards LDS slot `dst` (staged
+  // in `st` for fp32); commit: finish (fp32 register stores).  The caller
+  // waits for the memory counter and synchronises before the slot is read.
+  auto fetch1 = [&](bool is_v, u32x4 *st, char *dst, int kv0, int u) {
     const int so = __builtin_amdgcn_readfirstlane(kv0 * row_bytes);
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      if constexpr (C::DMA) {
-        const uint32_t la = lds0 + (uint32_t)(dst - smem) + 1024 * (C::WAVES * u + wave);
-        buf_load16_lds(is_v ? vwords : kwords, __builtin_amdgcn_readfirstlane(la), voff[u], so);
-      } else {
-        st[u] = buf_load16(is_v ? vrs : krs, voff[u], so);
-      }
+    if constexpr (C::DMA) {
+      const uint32_t la = lds0 + (uint32_t)(dst - smem) + 1024 * (C::WAVES * u + wave);
+      buf_load16_lds(is_v ? vwords : kwords, __builtin_amdgcn_readfirstlane(la), voff[u], so);
+    } else {
+      st[u] = buf_load16(is_v ? vrs : krs, voff[u], so);
     }
+  };
+  auto fetch = [&](bool is_v, u32x4 *st, char *dst, int kv0) {
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) fetch1(is_v, st, dst, kv0, u);
   };
   auto commit = [&](const u32x4 *st, char *dst) {
     if constexpr (!C::DMA) {
 #pragma unroll
       for (int u = 0; u < C::CPT; ++u) {
-        const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+        const int c = tid + C::NTHR * u, row = c / C::CPR, col = c - row * C::CPR;
         *reinterpret_cast<u32x4 *>(dst + row * C::PITCH + col * 16) = st[u];
       }
     }
   };
 
-  // Carried state (section "Incremental softmax tracking"): m_run is the
-  // reference point of the exponentials (a running max of scale*log2(e)*S,
-  // raised lazily), lpart this lane's share of the exponential sum (four
-  // independent partial sums), oacc the unnormalised output O^T.
-  float m_run = -INFINITY;
-  float lpart[4] = {0.f, 0.f, 0.f, 0.f};
-  f32x16 oacc[C::NOB];
+  // Carried state per query block (section "Incremental softmax tracking"):
+  // m_run is the reference point of the exponentials (a running max of
+  // scale*log2(e)*S, raised lazily), lpart this lane's share of the
+  // exponential sum (four independent partial sums), oacc the unnormalised
+  // output O^T.
+  float m_run[QB];
+  float lpart[QB][4];
+  f32x16 oacc[QB][C::NOB];
 #pragma unroll
-  for (int nb = 0; nb < C::NOB; ++nb) oacc[nb] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lpart[qb][q] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < C::NOB; ++nb) oacc[qb][nb] = f32x16{};
+  }
   const float c2 = p.scale_log2;
 
   // Tiles that no mask touches form a prefix of the list (tiles ascend): a key
@@ -248,8 +271,10 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
     n_full = min(ntiles, lim / C::BC);
   }
 
-  // Operand fragments.  K: rows = keys, 16 bytes per lane.  V^T: rows = keys
-  // in register order, through the transposing read.
+  // Operand fragments.  K fragment i (step s = i / NSB over d, key block
+  // sb = i % NSB): rows = keys, 16 bytes per lane.  V^T fragment (k, nb)
+  // (key block sb = k / PSTEPS, step t = k % PSTEPS, output block nb): rows =
+  // keys in register order, through the transposing read.
   auto kfrag = [&](const char *kl, int i) -> frag {
     const int s = i / NSB, sb = i - s * NSB;
     return lds_frag<T>(kl, LT::off(sb * 32 + l32, (h * (D / 2) + s * KPL) * E));
@@ -258,16 +283,17 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
     const int sb = k / C::PSTEPS, t = k - sb * C::PSTEPS;
     return regorder_frag<T, LT>(vl, sb * 32, t, nb * 32);
   };
-  constexpr int NS1 = NSB * C::PSTEPS;  // PV steps (C::NOB MFMAs each)
-  constexpr int NS2 = NSB * C::KSTEPS;  // score MFMAs
-  constexpr int NEL = NSB * 16;         // score elements per lane per tile
+  constexpr int NS1 = NSB * C::PSTEPS;   // PV steps
+  constexpr int NG1 = NS1 * C::NOB;      // PV groups (one V fragment, QB MFMAs each)
+  constexpr int NG2 = NSB * C::KSTEPS;   // score groups (one K fragment, QB MFMAs each)
+#define EL(a, e) a[(e) / 16][(e) % 16]
 
-  // Row sum: the four bf16/f16 pairs of a P fragment go to four independent
+  // Row sums: the four bf16/f16 pairs of a P fragment go to four independent
   // partial sums (v_dot2 with ones: the sum of exactly the rounded values the
   // MFMA consumes).
-  auto rowsum = [&](frag pb) {
+  auto rowsum = [&](int qb, frag pb) {
     if constexpr (KPL == 1) {
-      lpart[0] += pb;
+      lpart[qb][0] += pb;
     } else {
       typedef T t2 __attribute__((ext_vector_type(2)));
       const t2 one = {(T)1.0f, (T)1.0f};
@@ -275,74 +301,96 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
       for (int q = 0; q < 4; ++q) {
         const t2 v = {pb[2 * q], pb[2 * q + 1]};
         if constexpr (__is_same(T, __bf16))
-          lpart[q] = __builtin_amdgcn_fdot2_f32_bf16(v, one, lpart[q], false);
+          lpart[qb][q] = __builtin_amdgcn_fdot2_f32_bf16(v, one, lpart[qb][q], false);
         else
-          lpart[q] = __builtin_amdgcn_fdot2(v, one, lpart[q], false);
+          lpart[qb][q] = __builtin_amdgcn_fdot2(v, one, lpart[qb][q], false);
       }
     }
   };
 
-  // step 1: S^T = K_j Q_i^T for the tile whose K rows are at kl.  Steps over d
-  // alternate between the 32-key blocks so consecutive MFMAs are independent.
-  auto scores = [&](const char *kl, f32x16 (&sacc)[NSB]) {
+  // step 1: S^T = K_j Q_i^T for the tile whose K rows are at kl (blocks
+  // b = qb*NSB + sb).
+  auto scores = [&](const char *kl, f32x16 (&S)[NBLK]) {
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) sacc[sb] = f32x16{};
+    for (int b = 0; b < NBLK; ++b) S[b] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < NS2; ++i) {
+    for (int i = 0; i < NG2; ++i) {
       const int s = i / NSB, sb = i - s * NSB;
-      sacc[sb] = M::mma32(kfrag(kl, i), qf[s], sacc[sb]);
+      const frag a = kfrag(kl, i);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) S[qb * NSB + sb] = M::mma32(a, qf[qb][s], S[qb * NSB + sb]);
       FA_FENCE();  // bounds the operand reads in flight (register pressure)
     }
   };
-  // Masking of the tile at kv0 (invisible scores -> -inf).
-  auto apply_mask = [&](f32x16 (&sacc)[NSB], int kv0) {
-    // key kv0 + o is visible iff o < lim_o (one bound per lane)
-    const int lim_o = CAUSAL ? min(kv_len, qi + 1) - kv0 : kv_len - kv0;
-    const int o_h = 4 * h;  // reg_row(r, h) = reg_row(r, 0) + 4 h
+  // Masking of the tile at kv0 (invisible scores -> -inf): key kv0 + o is
+  // visible to the lane's query of block qb iff o < its bound.
+  auto apply_mask = [&](f32x16 (&S)[NBLK], int kv0) {
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qi = qw0 + 32 * qb + l32;
+      const int lim_o = (CAUSAL ? min(kv_len, qi + 1) : kv_len) - kv0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (!(sb * 32 + reg_row(r, 0) + o_h < lim_o)) sacc[sb][r] = -INFINITY;
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!(sb * 32 + reg_row(r, 0) + 4 * h < lim_o)) S[qb * NSB + sb][r] = -INFINITY;
+    }
   };
   // steps 2-3 for the scores in S: the row max over both half-waves (four
   // independent max chains), scaled by scale*log2(e).  The reference point
   // moves only when some lane's max passed it by more than the slack; then
   // the carried state -- O, the partial sums and the exponentials P of the
   // previous tile, not yet added to O -- is rescaled by exp2(old - new).
-  auto update_max = [&](f32x16 (&S)[NSB], f32x16 (&P)[NSB], auto masked) {
-    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  auto update_max = [&](f32x16 (&S)[NBLK], f32x16 (&P)[NBLK], auto masked) {
+    float mt[QB];
+    bool grow = false;
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) mx[e & 3] = fmaxf(mx[e & 3], S[e / 16][e % 16]);
-    float m = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-    m = fmaxf(m, xor32(m));
-    const float mt = (decltype(masked)::value && m == -INFINITY) ? -INFINITY : m * c2;
-    if (__ballot(mt > m_run + kMaxSlack) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      if (m_new != -INFINITY) {
-        const float alpha = fast_exp2(m_run - m_new);
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) lpart[q] *= alpha;
+      for (int e = 0; e < NSB * 16; ++e) mx[e & 3] = fmaxf(mx[e & 3], EL(S, qb * NSB * 16 + e));
+      float m = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+      m = fmaxf(m, xor32(m));
+      mt[qb] = (decltype(masked)::value && m == -INFINITY) ? -INFINITY : m * c2;
+      grow = grow || mt[qb] > m_run[qb] + kMaxSlack;
+    }
+    if (__ballot(grow) != 0) {
 #pragma unroll
-        for (int nb = 0; nb < C::NOB; ++nb)
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = fmaxf(m_run[qb], mt[qb]);
+        if (m_new != -INFINITY) {
+          const float alpha = fast_exp2(m_run[qb] - m_new);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+          for (int q = 0; q < 4; ++q) lpart[qb][q] *= alpha;
 #pragma unroll
-        for (int e = 0; e < NEL; ++e) P[e / 16][e % 16] *= alpha;
-        m_run = m_new;
+          for (int nb = 0; nb < C::NOB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha;
+#pragma unroll
+          for (int e = 0; e < NSB * 16; ++e) EL(P, qb * NSB * 16 + e) *= alpha;
+          m_run[qb] = m_new;
+        }
       }
     }
   };
-  // step 4: O_i^T += V_j^T P^T for P in `pacc`, plus the row sums.
-  auto pv = [&](const char *vl, const f32x16 (&pacc)[NSB]) {
+  // step 4: O_i^T += V_j^T P^T for P in `P`, plus the row sums.
+  auto pv = [&](const char *vl, const f32x16 (&P)[NBLK]) {
 #pragma unroll
     for (int k = 0; k < NS1; ++k) {
       const int sb = k / C::PSTEPS, t = k - sb * C::PSTEPS;
-      const frag pb = pack_frag<T>(pacc[sb], t * KPL);
-      rowsum(pb);
+      frag pb[QB];
 #pragma unroll
-      for (int nb = 0; nb < C::NOB; ++nb) oacc[nb] = M::mma32(vfrag(vl, k, nb), pb, oacc[nb]);
-      FA_FENCE();  // bounds the operand reads in flight (register pressure)
+      for (int qb = 0; qb < QB; ++qb) {
+        pb[qb] = pack_frag<T>(P[qb * NSB + sb], t * KPL);
+        rowsum(qb, pb[qb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < C::NOB; ++nb) {
+        const frag va = vfrag(vl, k, nb);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = M::mma32(va, pb[qb], oacc[qb][nb]);
+        FA_FENCE();  // bounds the operand reads in flight (register pressure)
+      }
     }
   };
 
@@ -353,15 +401,18 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   // Generic iteration: any mask, any visibility.  Straight-line code: a tile
   // that the wave cannot see is fully masked, so its exponentials are 0 and
   // its PV adds nothing; past the last tile everything is masked.
-  auto iter_any = [&](int j, auto first, f32x16 (&X)[NSB], f32x16 (&Y)[NSB]) {
+  auto iter_any = [&](int j, auto first, f32x16 (&X)[NBLK], f32x16 (&Y)[NBLK]) {
     fetch(true, stv, vslot(j), tile_start(j));
     fetch(false, stk, kslot(j), tile_start(min(j + 2, ntiles - 1)));
     if constexpr (!decltype(first)::value) pv(vslot(j - 1), Y);
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-    for (int e = 0; e < NEL; ++e) {
-      const float x = fast_exp2(fmaf(X[e / 16][e % 16], c2, -m_use));
-      X[e / 16][e % 16] = X[e / 16][e % 16] == -INFINITY ? 0.f : x;  // masked keys (also for scale 0)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+#pragma unroll
+      for (int e = qb * NSB * 16; e < (qb + 1) * NSB * 16; ++e) {
+        const float x = fast_exp2(fmaf(EL(X, e), c2, -m_use));
+        EL(X, e) = EL(X, e) == -INFINITY ? 0.f : x;  // masked keys (also for scale 0)
+      }
     }
     scores(kslot(j + 1), Y);
     apply_mask(Y, j + 1 < ntiles ? tile_start(j + 1) : kv_len);  // all masked past the end
@@ -372,55 +423,69 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
     __syncthreads();
   };
 
-  // Iteration j for unmasked tiles j and j+1 (both visible) with j >= 1:
-  //  A: PV MFMAs of tile j-1 | fragment packing, row sums, x*c - m of tile j
+  // Iteration j for unmasked tiles j and j+1 with j >= 1:
+  //  A: PV MFMAs of tile j-1 | packing and row sums of P_{j-1}, x*c - m of
+  //     tile j; the LDS-DMA of V_j and K_{j+2} is issued here too
   //  B: score MFMAs of tile j+1 | exponentials of tile j
   //  C: row max of tile j+1 and the (rare) rescale.
-  // Operand reads run one group (V) or two (K) ahead of their MFMA.  `par` is
-  // the parity of j (a compile-time constant in the unrolled loop, so every
-  // LDS address is a loop-invariant register plus an immediate).
-  auto iter_steady = [&](int j, auto par, f32x16 (&X)[NSB], f32x16 (&Y)[NSB]) {
+  // Operand reads run two groups ahead of their MFMA.  `par` is the parity of
+  // j (a compile-time constant in the unrolled loop, so every LDS address is
+  // a loop-invariant register plus an immediate).
+  auto iter_steady = [&](int j, auto par, f32x16 (&X)[NBLK], f32x16 (&Y)[NBLK]) {
     constexpr int P = decltype(par)::value;
-    fetch(true, stv, vslot(P), tile_start(j));
-    fetch(false, stk, kslot(P), tile_start(min(j + 2, ntiles - 1)));
     const char *vl = vslot(P ^ 1), *kl = kslot(P ^ 1);
-    const float m_use = m_run;  // finite: every lane sees a key of tile j
-    // ---- A
-    frag vf[2][C::NOB], pbf[2];
+    const int kv_v = tile_start(j), kv_k = tile_start(min(j + 2, ntiles - 1));
+    float m_use[QB];  // finite: every lane sees a key of tile j
 #pragma unroll
-    for (int nb = 0; nb < C::NOB; ++nb) vf[0][nb] = vfrag(vl, 0, nb);
-    pbf[0] = pack_frag<T>(Y[0], 0);
+    for (int qb = 0; qb < QB; ++qb) m_use[qb] = m_run[qb];
+    // ---- A
+    frag vf[3], pbf[2][QB];
+    auto vf_of = [&](int g) { return vfrag(vl, g / C::NOB, g % C::NOB); };
+    vf[0] = vf_of(0);
+    if (NG1 > 1) vf[1] = vf_of(1);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) pbf[0][qb] = pack_frag<T>(Y[qb * NSB], 0);
     FA_FENCE();
 #pragma unroll
-    for (int k = 0; k < NS1; ++k) {
-      const int cb = k & 1;
-      if (k + 1 < NS1) {
+    for (int g = 0; g < NG1; ++g) {
+      const int k = g / C::NOB, nb = g % C::NOB, cb = k & 1;
+      if (g + 2 < NG1) vf[(g + 2) % 3] = vf_of(g + 2);
 #pragma unroll
-        for (int nb = 0; nb < C::NOB; ++nb) vf[cb ^ 1][nb] = vfrag(vl, k + 1, nb);
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = M::mma32(vf[g % 3], pbf[cb][qb], oacc[qb][nb]);
+      // LDS-DMA of the next tiles, spread over the first groups
+#pragma unroll
+      for (int u = 0; u < C::CPT; ++u) {
+        if (g == u % NG1) fetch1(true, stv, vslot(P), kv_v, u);
+        if (g == (C::CPT + u) % NG1) fetch1(false, stk, kslot(P), kv_k, u);
+      }
+      if (nb == 0) {
+        if (k + 1 < NS1) {
+          const int sb = (k + 1) / C::PSTEPS, t = (k + 1) - sb * C::PSTEPS;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) pbf[cb ^ 1][qb] = pack_frag<T>(Y[qb * NSB + sb], t * KPL);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) rowsum(qb, pbf[cb][qb]);
       }
 #pragma unroll
-      for (int nb = 0; nb < C::NOB; ++nb) oacc[nb] = M::mma32(vf[cb][nb], pbf[cb], oacc[nb]);
-      if (k + 1 < NS1) {
-        const int sb = (k + 1) / C::PSTEPS, t = (k + 1) - sb * C::PSTEPS;
-        pbf[cb ^ 1] = pack_frag<T>(Y[sb], t * KPL);
-      }
-      rowsum(pbf[cb]);
-#pragma unroll
-      for (int e = k * NEL / NS1; e < (k + 1) * NEL / NS1; ++e) X[e / 16][e % 16] = fmaf(X[e / 16][e % 16], c2, -m_use);
+      for (int e = g * NEL / NG1; e < (g + 1) * NEL / NG1; ++e)
+        EL(X, e) = fmaf(EL(X, e), c2, -m_use[e / (NSB * 16)]);
       FA_FENCE();
     }
     // ---- B
     frag kf[3];
     kf[0] = kfrag(kl, 0);
-    if (NS2 > 1) kf[1] = kfrag(kl, 1);
+    if (NG2 > 1) kf[1] = kfrag(kl, 1);
     FA_FENCE();
 #pragma unroll
-    for (int i = 0; i < NS2; ++i) {
+    for (int i = 0; i < NG2; ++i) {
       const int s = i / NSB, sb = i - s * NSB;
-      if (i + 2 < NS2) kf[(i + 2) % 3] = kfrag(kl, i + 2);
-      Y[sb] = M::mma32(kf[i % 3], qf[s], s == 0 ? f32x16{} : Y[sb]);
+      if (i + 2 < NG2) kf[(i + 2) % 3] = kfrag(kl, i + 2);
 #pragma unroll
-      for (int e = i * NEL / NS2; e < (i + 1) * NEL / NS2; ++e) X[e / 16][e % 16] = fast_exp2(X[e / 16][e % 16]);
+      for (int qb = 0; qb < QB; ++qb)
+        Y[qb * NSB + sb] = M::mma32(kf[i % 3], qf[qb][s], s == 0 ? f32x16{} : Y[qb * NSB + sb]);
+#pragma unroll
+      for (int e = i * NEL / NG2; e < (i + 1) * NEL / NG2; ++e) EL(X, e) = fast_exp2(EL(X, e));
       FA_FENCE();
     }
     // ---- C
@@ -435,15 +500,15 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   // SB holds the current tile's scores and SA the previous tile's
   // exponentials at the top of every iteration (the two arrays trade roles
   // inside an iteration; `rotate` swaps them back where needed).
-  f32x16 SA[NSB], SB[NSB];
+  f32x16 SA[NBLK], SB[NBLK];
 #pragma unroll
-  for (int sb = 0; sb < NSB; ++sb) SA[sb] = f32x16{};
+  for (int b = 0; b < NBLK; ++b) SA[b] = f32x16{};
   auto rotate = [&]() {
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      const f32x16 t = SA[sb];
-      SA[sb] = SB[sb];
-      SB[sb] = t;
+    for (int b = 0; b < NBLK; ++b) {
+      const f32x16 t = SA[b];
+      SA[b] = SB[b];
+      SB[b] = t;
     }
   };
   if (ntiles > 0) {
@@ -456,7 +521,7 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
   // the loop; otherwise the compiler keeps them "pending" at the loop header.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (ntiles > 0) {  // tile 0 is visible to every wave
+  if (ntiles > 0) {
     scores(kslot(0), SB);
     apply_mask(SB, tile_start(0));
     update_max(SB, SA, ftrue{});
@@ -486,31 +551,37 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnParams p) {
     rotate();
   }
   if (ntiles > 0) pv(vslot(ntiles - 1), SA);
-  const float l_run = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+#undef EL
 
   // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2
-  const float l_tot = l_run + xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qi < N) {
-    T *orow = O + (int64_t)qi * p.sn;
 #pragma unroll
-    for (int nb = 0; nb < C::NOB; ++nb)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qw0 + 32 * qb + l32;
+    const float l_half = (lpart[qb][0] + lpart[qb][1]) + (lpart[qb][2] + lpart[qb][3]);
+    const float l_tot = l_half + xor32(l_half);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qi < N) {
+      T *orow = O + (int64_t)qi * p.sn;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = nb * 32 + 8 * i + 4 * h;
-        if constexpr (E == 4) {
-          f32x4 v = {oacc[nb][4 * i] * inv, oacc[nb][4 * i + 1] * inv, oacc[nb][4 * i + 2] * inv,
-                     oacc[nb][4 * i + 3] * inv};
-          *reinterpret_cast<f32x4 *>(orow + d0) = v;
-        } else {
-          typedef T t4 __attribute__((ext_vector_type(4)));
-          t4 v;
+      for (int nb = 0; nb < C::NOB; ++nb)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) v[jj] = (T)(oacc[nb][4 * i + jj] * inv);
-          *reinterpret_cast<t4 *>(orow + d0) = v;
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = nb * 32 + 8 * i + 4 * h;
+          if constexpr (E == 4) {
+            f32x4 v = {oacc[qb][nb][4 * i] * inv, oacc[qb][nb][4 * i + 1] * inv,
+                       oacc[qb][nb][4 * i + 2] * inv, oacc[qb][nb][4 * i + 3] * inv};
+            *reinterpret_cast<f32x4 *>(orow + d0) = v;
+          } else {
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            t4 v;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) v[jj] = (T)(oacc[qb][nb][4 * i + jj] * inv);
+            *reinterpret_cast<t4 *>(orow + d0) = v;
+          }
         }
-      }
-    if (h == 0) p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      if (h == 0)
+        p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
   }
 }
 
@@ -522,7 +593,7 @@ static hipError_t launch_fwd_t(const AttnParams &p, hipStream_t s) {
   AttnParams a = p;
   void *args[] = {&a};
   return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE>),
-                         dim3((unsigned)grid), dim3(256), args, 0, s);
+                         dim3((unsigned)grid), dim3(C::NTHR), args, 0, s);
 }
 
 template <typename T, int D>

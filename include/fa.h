@@ -126,9 +126,9 @@ fa_status_t fa_fwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
                                void *o, float *lse, void *stream);
 
 /* Size in bytes of the device workspace fa_bwd needs for problem p (0 if p is
- * invalid).  It holds one float32 per query row, rowsum(dO * O): O(N) extra
- * memory (summary page, "Complexity analysis": O(N) beyond inputs and
- * outputs). */
+ * invalid).  It holds two float32 per query row, rowsum(dO * O) and the saved
+ * LSE rescaled to base 2: O(N) extra memory (summary page, "Complexity
+ * analysis": O(N) beyond inputs and outputs). */
 size_t fa_bwd_workspace_bytes(const fa_problem_t *p);
 
 /* Backward pass: gradients of <dO, O> (summary page, "Key ideas",
@@ -159,11 +159,11 @@ fa_status_t fa_bwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
 
 /* Stages of the backward launch sequence (bit set for fa_bwd_ex). */
 typedef enum fa_bwd_stage {
-  FA_BWD_PRE = 1,    /* D = rowsum(dO * O) into the workspace                */
+  FA_BWD_PRE = 1,    /* D = rowsum(dO * O) and LSE*log2(e) into the workspace */
   FA_BWD_MAIN = 2,   /* key-stationary pass: recompute S, P per tile; write
-                        dK, dV (reads D)                                     */
+                        dK, dV (reads the workspace)                         */
   FA_BWD_DQ = 4,     /* query-stationary pass: recompute S, P per tile; write
-                        dQ (reads D; independent of FA_BWD_MAIN)             */
+                        dQ (reads the workspace; independent of FA_BWD_MAIN) */
   FA_BWD_ALL = 7
 } fa_bwd_stage_t;
 

@@ -100,7 +100,7 @@ def test_workspace_size_and_too_small(lib):
     p = prob()
     need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
     rows = 2 * 3 * 256
-    assert rows * 4 <= need <= rows * 4 + 256         # one float per row: O(N)
+    assert rows * 8 <= need <= rows * 8 + 512         # two floats per row: O(N)
     assert bwd(lib, p, ws_bytes=need - 1) == INVALID
 
 
