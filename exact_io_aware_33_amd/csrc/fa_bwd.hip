@@ -274,9 +274,10 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   auto slot = [&](int t) -> char * { return smem + (t & (C::NSLOT - 1)) * C::SLOT; };
   // fetch1: part u of query block t (clamped to the list; u = CPTQ is the
   // statistics); commit: finish the fp32 register staging before the barrier.
+  // Past the end of the list the last block is fetched again, into the
+  // block's own ring slot (free: its previous block was consumed).
   auto fetch1 = [&](int t, int u) {
-    t = min(t, nq - 1);
-    const int q0 = qblock_start(t);
+    const int q0 = qblock_start(min(t, nq - 1));
     const uint32_t la = lds0 + (uint32_t)(slot(t) - smem);
     if (u == C::CPTQ) {
       buf_load4_lds(statwords, __builtin_amdgcn_readfirstlane(la + ((wave & 1) ? C::D_OFF : C::LSE_OFF)),
@@ -299,7 +300,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   };
   auto commit = [&](int t) {
     if constexpr (!C::DMA) {
-      char *ql = slot(min(t, nq - 1));
+      char *ql = slot(t);
 #pragma unroll
       for (int u = 0; u < C::CPTQ; ++u) {
         const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
@@ -545,18 +546,23 @@ struct DqCfg {
   static constexpr int KPL = Mma<T>::KPL;
   static constexpr int WAVES = 4;
   static constexpr int BR = 32 * WAVES;           // queries per workgroup
-  static constexpr int BC = (E == 4) ? 32 : 64;   // keys per LDS tile
-  static constexpr int NSB = BC / 32;             // 32-key blocks per tile
+  static constexpr int BC = 32;                   // keys per tile
   static constexpr int NOB = D / 32;              // 32-wide blocks of dQ
   static constexpr int KSTEPS = D / (2 * KPL);    // MFMA steps over d
   static constexpr int PSTEPS = 16 / KPL;         // MFMA steps over 32 keys
   // K rows are read 16 bytes per lane (A operand of S^T) and through the
-  // transposing read (A operand of dQ^T): swizzled 16-bit rows as in bwd_main.
-  static constexpr int PITCH = (E == 4) ? D * E + 16 : D * E;
+  // transposing read (A operand of dQ^T): swizzled 16-bit rows as in bwd_main,
+  // filled by LDS-DMA; fp32 rows padded and staged through registers.
+  static constexpr bool DMA = (E == 2);
+  static constexpr int ROWB = D * E;
+  static constexpr int PITCH = DMA ? ROWB : ROWB + 16;
   static constexpr int KTILE = BC * PITCH;
-  static constexpr int TILE_BYTES = 2 * KTILE;    // one stage: K then V
-  static constexpr int CPR = D * E / 16;
+  static constexpr int SLOT = 2 * KTILE;          // K tile, then V tile
+  static constexpr int NSLOT = 4;                 // ring of key tiles in LDS
+  static constexpr int AHEAD = 3;                 // tiles requested ahead
+  static constexpr int CPR = ROWB / 16;
   static constexpr int CPT = BC * CPR / (64 * WAVES);
+  static constexpr int FETCH_OPS = 2 * CPT;       // vector-memory ops per wave per tile
   static_assert(BC * CPR % (64 * WAVES) == 0, "tile must split evenly");
 };
 
@@ -566,13 +572,14 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = C::KPL, E = C::E;
-  using LK = Layout<C::PITCH, D * E, E != 4>;
+  using LK = Layout<C::PITCH, C::ROWB, C::DMA>;
+  using ftrue = std::integral_constant<bool, true>;
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSLOT * C::SLOT];
   __shared__ uint16_t blist[SPARSE ? kMaxMaskBlocksB : 1];
   __shared__ int nlist_s;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const int N = p.N;
   const int nqt = (N + C::BR - 1) / C::BR;
@@ -647,7 +654,9 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
     n_full = min(ntiles, lim / C::BC);
   }
 
-  // ---- this wave's Q and dO rows (B operands), LSE and D of the lane's query
+  // ---- this wave's Q and dO rows (B operands), lse*log2(e) and D of the
+  // lane's query.  dP^T accumulates onto -D (the first MFMA takes it as its
+  // addend), so the MFMA result is already dP - D.
   frag qf[C::KSTEPS], gf[C::KSTEPS];
   float lse2 = INFINITY, dl = 0.f;
   if (qi < N) {
@@ -667,36 +676,64 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
       gf[s] = frag{};
     }
   }
+  f32x16 negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -dl;
 
-  // ---- K/V staging (buffer loads -> registers -> LDS, double buffer)
+  // ---- key tiles into the LDS ring (tile t -> slot t % NSLOT): buffer loads
+  // with the tile start in the scalar offset, rows past N read as zeros
+  // (16-bit: LDS-DMA, fp32: through registers).
   const uint32_t kv_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, kv_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, kv_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, kv_bytes), vrs = make_rsrc(V, kv_bytes);
+  const i32x4 kwords = rsrc_words(K, kv_bytes), vwords = rsrc_words(V, kv_bytes);
+  const uint32_t lds0 = lds_addr(smem);
   const int row_bytes = (int)(p.sn * E);
   int voff[C::CPT];
 #pragma unroll
   for (int u = 0; u < C::CPT; ++u) {
-    const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-    voff[u] = row * row_bytes + col * 16;
+    if constexpr (C::DMA) {
+      const int c = 64 * (C::WAVES * u + wave) + lane;  // physical chunk
+      const int row = c / C::CPR, pc = c - row * C::CPR;
+      voff[u] = row * row_bytes + ((pc ^ LK::swz(row)) << 4);
+    } else {
+      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+      voff[u] = row * row_bytes + col * 16;
+    }
   }
-  u32x4 stk[C::CPT], stv[C::CPT];
-  auto load_tile = [&](int kv0) {
-    const int so = kv0 * row_bytes;
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
+  u32x4 stk[C::DMA ? 1 : C::CPT], stv[C::DMA ? 1 : C::CPT];
+  auto slot = [&](int t) -> char * { return smem + (t & (C::NSLOT - 1)) * C::SLOT; };
+  // Past the end of the list the last tile is fetched again, into the tile's
+  // own ring slot (free: its previous tile was consumed).
+  auto fetch1 = [&](int t, int u) {
+    const int so = __builtin_amdgcn_readfirstlane(tile_start(min(t, ntiles - 1)) * row_bytes);
+    if constexpr (C::DMA) {
+      const uint32_t la = lds0 + (uint32_t)(slot(t) - smem) + 1024 * (C::WAVES * u + wave);
+      buf_load16_lds(kwords, __builtin_amdgcn_readfirstlane(la), voff[u], so);
+      buf_load16_lds(vwords, __builtin_amdgcn_readfirstlane(la + C::KTILE), voff[u], so);
+    } else {
       stk[u] = buf_load16(krs, voff[u], so);
       stv[u] = buf_load16(vrs, voff[u], so);
     }
   };
-  auto store_tile = [&](int buf) {
-    char *kl = smem + buf * C::TILE_BYTES;
-    char *vl = kl + C::KTILE;
+  auto fetch = [&](int t) {
 #pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
-      *reinterpret_cast<u32x4 *>(kl + LK::off(row, col * 16)) = stk[u];
-      *reinterpret_cast<u32x4 *>(vl + LK::off(row, col * 16)) = stv[u];
+    for (int u = 0; u < C::CPT; ++u) fetch1(t, u);
+  };
+  auto commit = [&](int t) {
+    if constexpr (!C::DMA) {
+      char *kl = slot(t);
+#pragma unroll
+      for (int u = 0; u < C::CPT; ++u) {
+        const int c = tid + 256 * u, row = c / C::CPR, col = c - row * C::CPR;
+        *reinterpret_cast<u32x4 *>(kl + LK::off(row, col * 16)) = stk[u];
+        *reinterpret_cast<u32x4 *>(kl + C::KTILE + LK::off(row, col * 16)) = stv[u];
+      }
     }
+  };
+  auto sync_ring = [&]() {
+    if constexpr (C::DMA) __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::FETCH_OPS));
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
   f32x16 qacc[C::NOB];
@@ -704,68 +741,149 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
   for (int nb = 0; nb < C::NOB; ++nb) qacc[nb] = f32x16{};
   const float c2 = p.scale_log2;
 
-  auto tile = [&](const char *kl, const char *vl, int kv0, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    f32x16 sacc[C::NSB], dpacc[C::NSB];
+  // Fragments from a slot.  kvfrag(i): step s = i / 2 over d, tensor i % 2
+  // (0 = K for S^T, 1 = V for dP^T), rows = keys, 16 bytes per lane.
+  // ktfrag(g): K^T for step t = g / NOB over keys, output block nb = g % NOB,
+  // rows = keys in register order, through the transposing read.
+  auto kvfrag = [&](const char *kl, int i) -> frag {
+    return lds_frag<T>(kl + (i & 1) * C::KTILE, LK::off(l32, (h * (D / 2) + (i >> 1) * KPL) * E));
+  };
+  auto ktfrag = [&](const char *kl, int g) -> frag {
+    return regorder_frag<T, LK>(kl, 0, g / C::NOB, (g % C::NOB) * 32);
+  };
+  constexpr int NGA = 2 * C::KSTEPS;       // S^T / dP^T MFMAs per tile
+  constexpr int NGB = C::PSTEPS * C::NOB;  // dQ^T MFMAs per tile
+
+  // S^T = K Q^T and dP^T - D = V dO^T - D for the tile in `kl`.
+  auto sdp = [&](const char *kl, f32x16 &S, f32x16 &DP) {
+    S = f32x16{};
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-      sacc[sb] = f32x16{};
-      dpacc[sb] = f32x16{};
+    for (int i = 0; i < NGA; ++i) {
+      const int s = i >> 1;
+      if (i & 1) DP = M::mma32(kvfrag(kl, i), gf[s], s == 0 ? negd : DP);
+      else S = M::mma32(kvfrag(kl, i), qf[s], S);
+      FA_FENCE();  // bounds the operand reads in flight (register pressure)
+    }
+  };
+  // P = exp2(S*scale*log2e - lse2), dS^T = P (dP - D) in place (row r of the
+  // register layout); masked keys get 0.
+  auto grad_row = [&](f32x16 &S, f32x16 &DP, int r) {
+    const float pv = fast_exp2(fmaf(S[r], c2, -lse2));
+    DP[r] = pv * DP[r];
+  };
+  // dQ^T += K^T dS^T  (rows = d, column = this lane's query)
+  auto dqacc = [&](const char *kl, const f32x16 &DS) {
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        const int off = LK::off(sb * 32 + l32, (h * (D / 2) + s * KPL) * E);
-        sacc[sb] = M::mma32(lds_frag<T>(kl, off), qf[s], sacc[sb]);   // S^T = K Q^T
-        dpacc[sb] = M::mma32(lds_frag<T>(vl, off), gf[s], dpacc[sb]);  // dP^T = V dO^T
+    for (int t = 0; t < C::PSTEPS; ++t) {
+      const frag sf = pack_frag<T>(DS, t * KPL);
+#pragma unroll
+      for (int nb = 0; nb < C::NOB; ++nb) {
+        qacc[nb] = M::mma32(ktfrag(kl, t * C::NOB + nb), sf, qacc[nb]);
+        FA_FENCE();
       }
     }
-#pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(sacc[sb][r], c2, -lse2));
-        if constexpr (MASK) {
-          const int kk = kv0 + sb * 32 + reg_row(r, h);
-          if (!(kk < kv_len && (!CAUSAL || kk <= qi))) pv = 0.f;
-        }
-        dpacc[sb][r] = pv * (dpacc[sb][r] - dl);  // dS^T
-      }
-    // dQ^T += K^T dS^T  (rows = d, cols = this lane's query)
-#pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-      for (int t = 0; t < C::PSTEPS; ++t) {
-        const frag sfrag = pack_frag<T>(dpacc[sb], t * KPL);
-#pragma unroll
-        for (int nb = 0; nb < C::NOB; ++nb)
-          qacc[nb] = M::mma32(regorder_frag<T, LK>(kl, sb * 32, t, nb * 32), sfrag, qacc[nb]);
-      }
   };
 
+  // Every iteration j starts with (SX, DX) = (S^T_j, dP^T_j - D) and ends
+  // with (SY, DY) = (S^T_{j+1}, dP^T_{j+1} - D).
+  //
+  // Generic iteration: any mask, straight-line; past the last tile the
+  // next-tile products are computed on a repeated tile and never used.
+  auto iter_any = [&](int j, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
+    fetch(j + C::AHEAD);
+    const char *kl = slot(j), *kn = slot(j + 1);
+    const int lim_o = (CAUSAL ? min(kv_len, qi + 1) : kv_len) - tile_start(j);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      grad_row(SX, DX, r);
+      if (!(reg_row(r, 0) + 4 * h < lim_o)) DX[r] = 0.f;  // key kv0 + row invisible
+    }
+    sdp(kn, SY, DY);
+    dqacc(kl, DX);
+    commit(j + C::AHEAD);
+    sync_ring();
+  };
+  // Iteration j for an unmasked tile j with a successor: the NGA score / dP
+  // MFMAs of tile j+1 carry dS of the first 8 rows of tile j (then the
+  // packing of step 0), the first half of the NGB dQ MFMAs carry the last 8
+  // rows; operand reads two groups ahead; the next tile's LDS-DMA spread over
+  // the first groups.  `par` is j mod NSLOT (compile-time slot addresses).
+  auto iter_steady = [&](int j, auto par, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
+    constexpr int P = decltype(par)::value;
+    char *const kl = smem + P * C::SLOT;
+    char *const kn = smem + ((P + 1) % C::NSLOT) * C::SLOT;
+    frag af[3];
+    af[0] = kvfrag(kn, 0);
+    af[1] = kvfrag(kn, 1);
+    SY = f32x16{};
+    FA_FENCE();
+#pragma unroll
+    for (int g = 0; g < NGA; ++g) {
+      const int s = g >> 1;
+      if (g + 2 < NGA) af[(g + 2) % 3] = kvfrag(kn, g + 2);
+      if (g & 1) DY = M::mma32(af[g % 3], gf[s], s == 0 ? negd : DY);
+      else SY = M::mma32(af[g % 3], qf[s], SY);
+      if (g < C::CPT) fetch1(j + C::AHEAD, g);
+#pragma unroll
+      for (int r = 8 * g / NGA; r < 8 * (g + 1) / NGA; ++r) grad_row(SX, DX, r);
+      FA_FENCE();
+    }
+    frag tf[3], sf[2];
+    tf[0] = ktfrag(kl, 0);
+    if (NGB > 1) tf[1] = ktfrag(kl, 1);
+    sf[0] = pack_frag<T>(DX, 0);
+    FA_FENCE();
+#pragma unroll
+    for (int g = 0; g < NGB; ++g) {
+      const int t = g / C::NOB, nb = g % C::NOB;
+      if (g + 2 < NGB) tf[(g + 2) % 3] = ktfrag(kl, g + 2);
+      qacc[nb] = M::mma32(tf[g % 3], sf[t & 1], qacc[nb]);
+      if (g < NGB / 2) {
+#pragma unroll
+        for (int r = 8 + 8 * g / (NGB / 2); r < 8 + 8 * (g + 1) / (NGB / 2); ++r) grad_row(SX, DX, r);
+      }
+      if (g % C::NOB == C::NOB - 1 && t + 1 < C::PSTEPS) sf[(t + 1) & 1] = pack_frag<T>(DX, (t + 1) * KPL);
+      FA_FENCE();
+    }
+    commit(j + C::AHEAD);
+    sync_ring();
+  };
+
+  // ---- prologue
+  f32x16 SA, DA, SB, DB;
   if (ntiles > 0) {
-    load_tile(tile_start(0));
-    store_tile(0);
+#pragma unroll
+    for (int t = 0; t < C::AHEAD; ++t) {
+      fetch(t);
+      commit(t);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
-  int it = 0;
-  for (; it < n_full; ++it) {
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(tile_start(it + 1));
-    const char *kl = smem + (it & 1) * C::TILE_BYTES;
-    tile(kl, kl + C::KTILE, tile_start(it), std::integral_constant<bool, false>{});
-    if (has_next) store_tile((it + 1) & 1);
-    __syncthreads();
+  if (ntiles > 0) sdp(slot(0), SA, DA);
+  auto swap_ab = [&]() {
+    const f32x16 ts = SA, td = DA;
+    SA = SB;
+    DA = DB;
+    SB = ts;
+    DB = td;
+  };
+  // unmasked tiles first (a prefix), in trips of NSLOT; then the rest
+  int j = 0;
+  using s0 = std::integral_constant<int, 0>;
+  using s1 = std::integral_constant<int, 1>;
+  using s2 = std::integral_constant<int, 2>;
+  using s3 = std::integral_constant<int, 3>;
+  const int j_steady = min(n_full, ntiles - 1);  // tile j unmasked, j+1 exists
+  for (; j + C::NSLOT <= j_steady; j += C::NSLOT) {
+    iter_steady(j, s0{}, SA, DA, SB, DB);
+    iter_steady(j + 1, s1{}, SB, DB, SA, DA);
+    iter_steady(j + 2, s2{}, SA, DA, SB, DB);
+    iter_steady(j + 3, s3{}, SB, DB, SA, DA);
   }
-  for (; it < ntiles; ++it) {
-    const int kv0 = tile_start(it);
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(tile_start(it + 1));
-    const char *kl = smem + (it & 1) * C::TILE_BYTES;
-    if (!(CAUSAL && kv0 > qw0 + 31))
-      tile(kl, kl + C::KTILE, kv0, std::integral_constant<bool, true>{});
-    if (has_next) store_tile((it + 1) & 1);
-    __syncthreads();
+  for (; j < ntiles; ++j) {
+    iter_any(j, SA, DA, SB, DB);
+    swap_ab();
   }
 
   // ---- dQ = scale * (dS K)
@@ -784,7 +902,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
           typedef T t4 __attribute__((ext_vector_type(4)));
           t4 v;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (T)(qacc[nb][4 * i + j] * p.scale);
+          for (int jj = 0; jj < 4; ++jj) v[jj] = (T)(qacc[nb][4 * i + jj] * p.scale);
           *reinterpret_cast<t4 *>(qrow + d0) = v;
         }
       }
