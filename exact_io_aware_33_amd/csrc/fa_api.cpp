@@ -148,7 +148,7 @@ fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.ws_delta = static_cast<float *>(ws);
+  a.ws_negd = static_cast<float *>(ws);
   a.ws_lse2 = reinterpret_cast<float *>(static_cast<char *>(ws) + fa::ws_array_bytes(rows));
   if (sparse) {
     a.mask = mask;

@@ -44,7 +44,7 @@ constexpr int kMaxMaskBlocksB = 1024;
 
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O) and LSE * log2(e).  One thread per row.
+// 1. -D = -rowsum(dO * O) and LSE * log2(e).  One thread per row.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(AttnParams p) {
   const int64_t rows = (int64_t)p.B * p.H * p.N;
@@ -67,7 +67,8 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(AttnParams p) {
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc = fmaf((float)ta[e], (float)tb[e], acc);
   }
-  p.ws_delta[row] = acc;
+  // stored negated: the dP MFMAs accumulate onto it (acc = dP - D)
+  p.ws_negd[row] = -acc;
   // the saved statistics in the base-2 domain: P = exp2(S*scale*log2e - lse2);
   // a row that sees no key (LSE = -inf) gets +inf, so its P is 0
   const float l = p.lse[row];
@@ -95,7 +96,7 @@ struct BwdCfg {
   static constexpr int ROWB = D * E;
   static constexpr int PITCH = DMA ? ROWB : ROWB + 16;
   static constexpr int QBYTES = BQ * PITCH;     // one Q (or dO) block
-  // One slot: Q block, dO block, then lse*log2(e) and D of 64 rows (one
+  // One slot: Q block, dO block, then lse*log2(e) and -D of 64 rows (one
   // 4-byte LDS-DMA; the first 32 belong to the block).
   static constexpr int LSE_OFF = 2 * QBYTES, D_OFF = LSE_OFF + 256;
   static constexpr int SLOT = 2 * QBYTES + 512;
@@ -141,7 +142,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   T *dK = static_cast<T *>(p.dk) + base;
   T *dV = static_cast<T *>(p.dv) + base;
   const float *LSE = p.lse + (int64_t)bh * N;
-  const float *Dl = p.ws_delta + (int64_t)bh * N;
+  const float *negD = p.ws_negd + (int64_t)bh * N;
 
   int kv_len = N;
   if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
@@ -247,14 +248,14 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
 
   // ---- query blocks into the LDS ring (block t -> slot t % NSLOT).  Q, dO:
   // buffer loads with the block start in the scalar offset, rows past N read
-  // as zeros (16-bit: LDS-DMA, fp32: through registers).  lse*log2(e) and D
+  // as zeros (16-bit: LDS-DMA, fp32: through registers).  lse*log2(e) and -D
   // from the workspace by 4-byte LDS-DMA (waves 0 and 2 the one, 1 and 3 the
   // other, so every wave issues the same number of operations).  Rows past N
   // read zeros there too: with zero Q and dO rows they add nothing to dK, dV.
   const uint32_t q_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, q_bytes), dors = make_rsrc(dO, q_bytes);
   const i32x4 qwords = rsrc_words(Q, q_bytes), dowords = rsrc_words(dO, q_bytes);
-  const i32x4 statwords = (wave & 1) ? rsrc_words(Dl, (uint32_t)N * 4u)
+  const i32x4 statwords = (wave & 1) ? rsrc_words(negD, (uint32_t)N * 4u)
                                      : rsrc_words(p.ws_lse2 + (int64_t)bh * N, (uint32_t)N * 4u);
   const uint32_t lds0 = lds_addr(smem);
   const int row_bytes = (int)(p.sn * E);
@@ -334,12 +335,37 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   };
   constexpr int NGA = 2 * C::KSTEPS;            // S / dP MFMAs per block
   constexpr int NGB = 2 * C::TSTEPS * C::NOB;   // dV / dK MFMAs per block
+  // Issue order of the S / dP MFMAs: three S steps first (so the -D addend of
+  // the first dP step has time to arrive from LDS), then dP and S alternate.
+  // Returns the qfrag index 2 s + tensor.
+  auto sdp_order = [](int g) constexpr -> int {
+    constexpr int K = C::KSTEPS;
+    if (g < 3) return 2 * g;
+    if (g < 3 + 2 * (K - 3)) {
+      const int k = g - 3;
+      return (k & 1) ? 2 * (3 + k / 2) : 2 * (k / 2) + 1;
+    }
+    return 2 * ((K - 3) + (g - 3 - 2 * (K - 3))) + 1;
+  };
+  // -D of the block's 32 rows in register order (the addend of the first dP
+  // MFMA: the accumulator then holds dP - D)
+  auto load_negd = [&](const char *qs) -> f32x16 {
+    const float *dd = reinterpret_cast<const float *>(qs + C::D_OFF);
+    f32x16 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(dd + 8 * q + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[4 * q + j] = v[j];
+    }
+    return r;
+  };
 
   // S = Q K^T, dP = dO V^T for the block in `ql` (rows = queries in register
   // order, column = this lane's key).
   auto sdp = [&](const char *ql, f32x16 &S, f32x16 &DP) {
     S = f32x16{};
-    DP = f32x16{};
+    DP = load_negd(ql);
 #pragma unroll
     for (int i = 0; i < NGA; ++i) {
       const int s = i >> 1;
@@ -348,16 +374,15 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
       FA_FENCE();  // bounds the operand reads in flight (register pressure)
     }
   };
-  // P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - D), in place; with
-  // MASK, invisible (query, key) pairs get P = dS = 0.
+  // P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - D) with DP = dP - D
+  // already, in place; with MASK, invisible (query, key) pairs get
+  // P = dS = 0.
   auto softmax_grad = [&](const char *ql, int q0, f32x16 &S, f32x16 &DP, auto masked) {
     const float *ll = reinterpret_cast<const float *>(ql + C::LSE_OFF);
-    const float *dd = reinterpret_cast<const float *>(ql + C::D_OFF);
     const int lim_q = CAUSAL ? key - q0 : -1;  // query row qr visible iff qr >= lim_q
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ll + 8 * i + 4 * h);
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dd + 8 * i + 4 * h);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * i + j;
@@ -366,7 +391,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
           if (!(key < kv_len && reg_row(r, h) >= lim_q)) pv = 0.f;
         }
         S[r] = pv;
-        DP[r] = pv * (DP[r] - d4[j]);
+        DP[r] = pv * DP[r];
       }
     }
   };
@@ -416,33 +441,29 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     char *const ql = smem + P * C::SLOT;
     char *const qn = smem + ((P + 1) % C::NSLOT) * C::SLOT;
     const float *ll = reinterpret_cast<const float *>(ql + C::LSE_OFF);
-    const float *dd = reinterpret_cast<const float *>(ql + C::D_OFF);
-    f32x4 l4[2], d4[2];
+    f32x4 l4[2];
     // P, dS of row r (quad q = r / 4 prefetched one quad ahead)
     auto row = [&](int r) {
       const int q = r >> 2, j = r & 3;
-      if (j == 0 && q + 1 < 4) {
+      if (j == 0 && q + 1 < 4)
         l4[(q + 1) & 1] = *reinterpret_cast<const f32x4 *>(ll + 8 * (q + 1) + 4 * h);
-        d4[(q + 1) & 1] = *reinterpret_cast<const f32x4 *>(dd + 8 * (q + 1) + 4 * h);
-      }
       const float pv = fast_exp2(fmaf(SX[r], c2, -l4[q & 1][j]));
       SX[r] = pv;
-      DX[r] = pv * (DX[r] - d4[q & 1][j]);
+      DX[r] = pv * DX[r];
     };
     // ---- score / dP MFMAs of block i+1
     frag af[3];
-    af[0] = qfrag(qn, 0);
-    af[1] = qfrag(qn, 1);
+    af[0] = qfrag(qn, sdp_order(0));
+    af[1] = qfrag(qn, sdp_order(1));
+    const f32x16 negd_n = load_negd(qn);
     l4[0] = *reinterpret_cast<const f32x4 *>(ll + 4 * h);
-    d4[0] = *reinterpret_cast<const f32x4 *>(dd + 4 * h);
     SY = f32x16{};
-    DY = f32x16{};
     FA_FENCE();
 #pragma unroll
     for (int g = 0; g < NGA; ++g) {
-      const int s = g >> 1;
-      if (g + 2 < NGA) af[(g + 2) % 3] = qfrag(qn, g + 2);
-      if (g & 1) DY = M::mma32(af[g % 3], vf[s], DY);
+      const int fi = sdp_order(g), s = fi >> 1;
+      if (g + 2 < NGA) af[(g + 2) % 3] = qfrag(qn, sdp_order(g + 2));
+      if (fi & 1) DY = M::mma32(af[g % 3], vf[s], s == 0 ? negd_n : DY);
       else SY = M::mma32(af[g % 3], kf[s], SY);
       if (g <= C::CPTQ) fetch1(i + C::AHEAD, g);
 #pragma unroll
@@ -567,7 +588,8 @@ struct DqCfg {
 };
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
+// d = 128: at most 256 VGPRs, so that two waves share each SIMD
+__global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnParams p) {
   using C = DqCfg<T, D>;
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -658,7 +680,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
   // lane's query.  dP^T accumulates onto -D (the first MFMA takes it as its
   // addend), so the MFMA result is already dP - D.
   frag qf[C::KSTEPS], gf[C::KSTEPS];
-  float lse2 = INFINITY, dl = 0.f;
+  float lse2 = INFINITY, negdl = 0.f;
   if (qi < N) {
     const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
     const T *grow = dO + (int64_t)qi * p.sn + h * (D / 2);
@@ -668,7 +690,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
       gf[s] = *reinterpret_cast<const frag *>(grow + s * KPL);
     }
     lse2 = p.ws_lse2[(int64_t)bh * N + qi];  // +inf when no key is visible: P = 0
-    dl = p.ws_delta[(int64_t)bh * N + qi];
+    negdl = p.ws_negd[(int64_t)bh * N + qi];
   } else {
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
@@ -678,7 +700,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnParams p) {
   }
   f32x16 negd;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) negd[r] = -dl;
+  for (int r = 0; r < 16; ++r) negd[r] = negdl;
 
   // ---- key tiles into the LDS ring (tile t -> slot t % NSLOT): buffer loads
   // with the tile start in the scalar offset, rows past N read as zeros

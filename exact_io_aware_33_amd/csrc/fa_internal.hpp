@@ -20,7 +20,7 @@ struct AttnParams {
   const void *o_in;   // forward output, read by the preprocess kernel
   const void *dout;
   void *dq, *dk, *dv;
-  float *ws_delta;    // [B*H*N]  rowsum(dO * O)
+  float *ws_negd;     // [B*H*N]  -D = -rowsum(dO * O)
   float *ws_lse2;     // [B*H*N]  LSE * log2(e); +inf for rows that see no key
   // problem
   int32_t B, H, N, d;
@@ -44,7 +44,7 @@ hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, unsigned 
                       hipStream_t s);
 
 // Backward workspace: two floats per query row, each array 256-byte aligned:
-// D = rowsum(dO * O), then LSE in the base-2 domain.
+// -D = -rowsum(dO * O), then LSE in the base-2 domain.
 inline size_t ws_array_bytes(int64_t rows) { return (size_t)((rows * 4 + 255) / 256 * 256); }
 inline size_t ws_total_bytes(int64_t rows) { return 2 * ws_array_bytes(rows); }
 
