@@ -47,10 +47,12 @@ template <typename T, int D, bool SPARSE>
 struct FwdCfg {
   static constexpr int E = sizeof(T);
   static constexpr int KPL = Mma<T>::KPL;
-  // 32-query blocks per wavefront: two for 16-bit d = 64 (each K / V
-  // fragment feeds two MFMAs, halving LDS reads per MFMA), one otherwise
-  // (d = 128 needs the registers for its output accumulators).
-  static constexpr int QB = (E == 2 && D == 64) ? 2 : 1;
+  // 32-query blocks per wavefront.  Two (each K / V fragment feeding two
+  // MFMAs, half the LDS reads per MFMA, 2-wave workgroups) were measured
+  // slower on gfx950 than one block per wave at three waves per SIMD
+  // (16K causal 0.69 vs 0.65 ms): LDS bandwidth is not what limits this
+  // kernel.  The code keeps QB general.
+  static constexpr int QB = 1;
   static constexpr int WAVES = 4 / QB;
   static constexpr int NTHR = 64 * WAVES;
   static constexpr int QPW = 32 * QB;             // queries per wavefront
@@ -93,7 +95,9 @@ constexpr float kMaxSlack = 8.0f;
 #define FA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR)) fwd_kernel(AttnParams p) {
+// d = 64: registers bounded for three waves per SIMD (the few spills this
+// costs sit outside the tile loops).
+__global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? 3 : 1)) fwd_kernel(AttnParams p) {
   using C = FwdCfg<T, D, SPARSE>;
   using M = Mma<T>;
   using frag = typename M::frag;
