@@ -11,10 +11,14 @@ from them.
 * :mod:`oracle.streaming` -- the pages' block-by-block recurrence (running max,
   running sum, rescaled output), used only to pin the definition against the
   method's own algorithm.
+* :mod:`oracle.dropout` -- the Philox4x32-10 generator and the dropout keep
+  mask (used through the ``dropout=`` argument of the attention functions).
 """
 from .attention import (allowed_mask, forward, backward, forward_rows,
                         gradients_sampled, probabilities)
 from .streaming import merge_stats, streaming_forward
+from .dropout import keep_mask, keep_scale, drop_threshold, philox4x32_10
 
 __all__ = ["allowed_mask", "forward", "backward", "forward_rows",
-           "probabilities", "gradients_sampled", "merge_stats", "streaming_forward"]
+           "probabilities", "gradients_sampled", "merge_stats", "streaming_forward",
+           "keep_mask", "keep_scale", "drop_threshold", "philox4x32_10"]

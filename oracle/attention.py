@@ -23,6 +23,14 @@ What is computed, and where the pages define it
       dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
       dS = P * (dP - D 1^T),  dQ = scale dS K,  dK = scale dS^T Q.
 
+* Dropout (named in the kernel-fusion bullet of the same section) is
+  optional: ``dropout=(p, seed, offset)`` applies the keep mask Z of
+  :mod:`oracle.dropout` (kept entries scaled by 1 / (1 - p)) to P before the
+  product with V:  O = (P * Z) V, LSE unchanged (statistics of the undropped
+  softmax).  Gradients of <dO, O> with the mask held fixed:
+      dV = (P * Z)^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
+      dS = P * (Z * dP - D 1^T),  dQ = scale dS K,  dK = scale dS^T Q.
+
 Conventions: arrays are float64 numpy arrays shaped [B, H, N, d]; ``scale`` is
 applied as a float64 number (callers pass the float32 value the GPU uses); a
 query row with no visible key has O = 0, LSE = -inf and zero gradients.
@@ -32,6 +40,8 @@ chunk still forms its full score rows.
 from __future__ import annotations
 
 import numpy as np
+
+from .dropout import keep_mask, keep_scale
 
 __all__ = ["allowed_mask", "forward", "forward_rows", "backward", "probabilities",
            "gradients_sampled"]
@@ -78,8 +88,16 @@ def _row_softmax_stats(s):
     return m, l, valid, e
 
 
+def _z(bh, rows, cols, dropout):
+    """Dropout factor Z (0 or 1/(1-p)) for the given rows / columns, or None."""
+    if dropout is None:
+        return None
+    p, seed, offset = dropout
+    return keep_mask(bh, rows, cols, p, seed, offset) * keep_scale(p)
+
+
 def forward_rows(q, k, v, scale, rows, *, causal=False, key_len=None,
-                 block_mask=None, mb=128):
+                 block_mask=None, mb=128, dropout=None, bh=0):
     """O and LSE of one (batch, head) for the query indices ``rows`` only.
 
     q: [N, d] (only ``rows`` are read), k, v: [N, d].  Returns (o [R, d],
@@ -96,7 +114,8 @@ def forward_rows(q, k, v, scale, rows, *, causal=False, key_len=None,
     s = np.where(a, s, -np.inf)
     m, l, valid, e = _row_softmax_stats(s)
     p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
-    o = p @ v
+    z = _z(bh, rows, np.arange(N), dropout)
+    o = (p if z is None else p * z) @ v
     lse = np.where(valid, m + np.log(np.where(valid, l, 1.0)), -np.inf)
     return o, lse
 
@@ -110,7 +129,7 @@ def _lens(key_lens, B):
 
 
 def forward(q, k, v, scale, *, causal=False, key_lens=None, block_mask=None,
-            mb=128, chunk=1024):
+            mb=128, chunk=1024, dropout=None):
     """Exact attention forward.  Returns (O [B,H,N,dv], LSE [B,H,N]) in fp64.
 
     N is the number of query rows; K and V may hold a different number of
@@ -127,7 +146,7 @@ def forward(q, k, v, scale, *, causal=False, key_lens=None, block_mask=None,
                 rows = np.arange(r0, min(N, r0 + chunk))
                 ob, lb = forward_rows(q[b, h], k[b, h], v[b, h], scale, rows,
                                       causal=causal, key_len=lens[b],
-                                      block_mask=bm, mb=mb)
+                                      block_mask=bm, mb=mb, dropout=dropout, bh=b * H + h)
                 o[b, h, rows] = ob
                 lse[b, h, rows] = lb
     return o, lse
@@ -150,7 +169,7 @@ def probabilities(q, k, scale, *, causal=False, key_len=None, block_mask=None, m
 
 
 def backward(q, k, v, do, scale, *, causal=False, key_lens=None, block_mask=None,
-             mb=128, chunk=1024, return_aux=False):
+             mb=128, chunk=1024, return_aux=False, dropout=None):
     """Analytic gradients of <dO, O> w.r.t. Q, K, V (fp64).
 
     Returns (dq, dk, dv); with ``return_aux`` also (o, lse, D_from_p, D_from_o),
@@ -178,13 +197,16 @@ def backward(q, k, v, do, scale, *, causal=False, key_lens=None, block_mask=None
                 s = np.where(a, s, -np.inf)
                 m, l, valid, e = _row_softmax_stats(s)
                 p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
-                oc = p @ vb
+                z = _z(b * H + h, rows, np.arange(N), dropout)
+                pz = p if z is None else p * z
+                oc = pz @ vb
                 dpc = dob[rows] @ vb.T
-                Dp = np.sum(p * dpc, axis=1)
-                ds = p * (dpc - Dp[:, None])
+                zdp = dpc if z is None else z * dpc
+                Dp = np.sum(p * zdp, axis=1)
+                ds = p * (zdp - Dp[:, None])
                 dq[b, h, rows] = float(scale) * (ds @ kb)
                 dk[b, h] += float(scale) * (ds.T @ qb[rows])
-                dv[b, h] += p.T @ dob[rows]
+                dv[b, h] += pz.T @ dob[rows]
                 o[b, h, rows] = oc
                 lse[b, h, rows] = np.where(valid, m + np.log(np.where(valid, l, 1.0)), -np.inf)
                 D_p[b, h, rows] = Dp
@@ -195,7 +217,7 @@ def backward(q, k, v, do, scale, *, causal=False, key_lens=None, block_mask=None
 
 
 def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=None,
-                      block_mask=None, mb=128, chunk=1024):
+                      block_mask=None, mb=128, chunk=1024, dropout=None, bh=0):
     """Exact gradients of one (batch, head) at selected rows / columns only.
 
     Same definition as :func:`backward`; used at sizes where the full N x d
@@ -221,6 +243,9 @@ def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=N
         m, l, valid, e = _row_softmax_stats(s)
         p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
         dp = do[rr] @ v.T
+        z = _z(bh, rr, np.arange(N), dropout)
+        if z is not None:
+            dp = z * dp
         lse_all[rr] = np.where(valid, m + np.log(np.where(valid, l, 1.0)), -np.inf)
         D_all[rr] = np.sum(p * dp, axis=1)
     # selected rows: O, LSE, dQ
@@ -230,8 +255,10 @@ def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=N
     lr = lse_all[rows]
     fin = np.isfinite(lr)
     p = np.where(fin[:, None], np.exp(s - np.where(fin, lr, 0.0)[:, None]), 0.0)
-    o_rows = p @ v
-    ds = p * ((do[rows] @ v.T) - D_all[rows][:, None])
+    z = _z(bh, rows, np.arange(N), dropout)
+    o_rows = (p if z is None else p * z) @ v
+    dpr = do[rows] @ v.T
+    ds = p * ((dpr if z is None else z * dpr) - D_all[rows][:, None])
     dq_rows = float(scale) * (ds @ k)
     # selected columns: dK, dV
     dk_cols = np.zeros((cols.size, q.shape[1]))
@@ -244,7 +271,9 @@ def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=N
         lc = lse_all[rr]
         fin = np.isfinite(lc)
         p = np.where(fin[:, None], np.exp(s - np.where(fin, lc, 0.0)[:, None]), 0.0)
-        ds = p * ((do[rr] @ v[cols].T) - D_all[rr][:, None])
+        z = _z(bh, rr, cols, dropout)
+        dpc = do[rr] @ v[cols].T
+        ds = p * ((dpc if z is None else z * dpc) - D_all[rr][:, None])
         dk_cols += float(scale) * (ds.T @ q[rr])
-        dv_cols += p.T @ do[rr]
+        dv_cols += (p if z is None else p * z).T @ do[rr]
     return o_rows, lse_all[rows], dq_rows, dk_cols, dv_cols
