@@ -71,13 +71,16 @@ def keep_scale(p):
 def keep_mask(bh, rows, cols, p, seed, offset=0):
     """Boolean [len(rows), len(cols)]: True where key cols[c] is kept for
     query rows[r] in head bh (see the module docstring for the mapping)."""
-    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 1)
-    cols = np.asarray(cols, dtype=np.int64).reshape(1, -1)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    cols = np.asarray(cols, dtype=np.int64).reshape(-1)
     t = drop_threshold(p)
     seed = int(seed)
-    words = philox4x32_10(rows // 4, cols // 4, int(bh), int(offset) & 0xFFFFFFFF,
-                          seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    w = np.broadcast_to(rows % 4, (rows.shape[0], cols.shape[1]))
-    word = np.choose(w, words)
-    byte = (word >> (np.uint64(8) * (cols % 4).astype(np.uint64))) & np.uint64(0xFF)
+    # one generator call per distinct 4x4 block, then each element picks its
+    # word (query) and byte (key) out of its block's output
+    qblk, qidx = np.unique(rows // 4, return_inverse=True)
+    kblk, kidx = np.unique(cols // 4, return_inverse=True)
+    words = np.stack(philox4x32_10(qblk[:, None], kblk[None, :], int(bh), int(offset) & 0xFFFFFFFF,
+                                   seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
+    word = words[(rows % 4)[:, None], qidx.reshape(-1)[:, None], kidx.reshape(-1)[None, :]]
+    byte = (word >> (np.uint64(8) * (cols % 4).astype(np.uint64))[None, :]) & np.uint64(0xFF)
     return byte >= np.uint64(t)

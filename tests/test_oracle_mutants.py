@@ -64,9 +64,9 @@ DROP_MUTANTS = [
     ("key never bumped", DROP_SRC, "        if r < 9:\n", "        if False:\n"),
     ("Philox products swapped", DROP_SRC, "c = [hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0]",
      "c = [hi0 ^ c[1] ^ k0, lo0, hi1 ^ c[3] ^ k1, lo1]"),
-    ("counter blocks transposed", DROP_SRC, "philox4x32_10(rows // 4, cols // 4, int(bh)",
-     "philox4x32_10(cols // 4, rows // 4, int(bh)"),
-    ("word chosen by the key", DROP_SRC, "w = np.broadcast_to(rows % 4,", "w = np.broadcast_to(cols % 4,"),
+    ("counter blocks transposed", DROP_SRC, "philox4x32_10(qblk[:, None], kblk[None, :], int(bh)",
+     "philox4x32_10(kblk[None, :], qblk[:, None], int(bh)"),
+    ("word chosen by the key", DROP_SRC, "word = words[(rows % 4)[:, None],", "word = words[(cols % 4)[None, :],"),
     ("threshold truncated", DROP_SRC, "round(float(p) * 256.0)", "int(float(p) * 256.0)"),
     ("keep on byte > t", DROP_SRC, "return byte >= np.uint64(t)", "return byte > np.uint64(t)"),
     ("seed high word dropped", DROP_SRC, "seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)",
