@@ -8,6 +8,11 @@ if the library is missing, the call raises.
 
 Tensors are ``[B, H, N, d]`` views with unit stride along d; Q, K, V, O, dO
 (and the gradients this module allocates) share one set of strides.
+
+Dropout: every entry point takes ``dropout_p`` (0 = none), ``dropout_seed``
+(64-bit Philox key) and ``dropout_offset`` (32-bit counter word); the backward
+call must repeat the forward's values (the keep mask is regenerated, never
+stored).
 """
 from __future__ import annotations
 
@@ -47,7 +52,7 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _problem(q, scale, causal, key_lens):
+def _problem(q, scale, causal, key_lens, dropout_p=0.0, dropout_seed=0, dropout_offset=0):
     if q.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
     if q.dtype not in _DTYPES:
@@ -61,10 +66,14 @@ def _problem(q, scale, causal, key_lens):
         if key_lens.dtype != torch.int32 or key_lens.device != q.device or key_lens.numel() != B:
             raise ValueError("key_lens must be an int32 [B] tensor on the device of q")
         key_lens = key_lens.contiguous()
+    if not 0 <= int(dropout_seed) < 2 ** 64 or not 0 <= int(dropout_offset) < 2 ** 32:
+        raise ValueError("dropout_seed must fit 64 bits and dropout_offset 32 bits (unsigned)")
     p = FaProblem(batch=B, heads=H, seqlen=N, head_dim=d,
                   stride_b=q.stride(0), stride_h=q.stride(1), stride_n=q.stride(2),
                   scale=float(scale), causal=1 if causal else 0, dtype=_DTYPES[q.dtype],
-                  key_lens=None if key_lens is None else key_lens.data_ptr())
+                  key_lens=None if key_lens is None else key_lens.data_ptr(),
+                  dropout_p=float(dropout_p), dropout_offset=int(dropout_offset),
+                  dropout_seed=int(dropout_seed))
     return p, key_lens
 
 
@@ -79,10 +88,11 @@ def _empty_like_layout(q):
     return torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
 
 
-def fa_fwd(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=None):
+def fa_fwd(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=None,
+           dropout_p=0.0, dropout_seed=0, dropout_offset=0):
     """Exact attention forward; returns (O, LSE).  Calls fa_fwd."""
     _same_layout(q, k, v)
-    p, kl = _problem(q, scale, causal, key_lens)
+    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
     o = _empty_like_layout(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     _same_layout(q, o)
@@ -92,11 +102,12 @@ def fa_fwd(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=No
 
 
 def fa_fwd_blocksparse(q, k, v, block_mask, *, mask_block=128, scale=None, causal=False,
-                       key_lens=None, out=None, lse=None):
+                       key_lens=None, out=None, lse=None, dropout_p=0.0, dropout_seed=0,
+                       dropout_offset=0):
     """Block-sparse forward; ``block_mask`` is uint8 [N/mb, N/mb] (shared by all heads)
     or [H, N/mb, N/mb].  Returns (O, LSE).  Calls fa_fwd_blocksparse."""
     _same_layout(q, k, v)
-    p, kl = _problem(q, scale, causal, key_lens)
+    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
     bm, hstride = _mask(block_mask, q)
     o = _empty_like_layout(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
@@ -143,10 +154,10 @@ def _bwd_outputs(q, workspace, p, grads):
 
 
 def fa_bwd(q, k, v, o, lse, do, *, scale=None, causal=False, key_lens=None, workspace=None,
-           dq=None, dk=None, dv=None):
+           dq=None, dk=None, dv=None, dropout_p=0.0, dropout_seed=0, dropout_offset=0):
     """Gradients (dQ, dK, dV) of <dO, O>.  Calls fa_bwd."""
     _same_layout(q, k, v, o, do)
-    p, kl = _problem(q, scale, causal, key_lens)
+    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
     dq, dk, dv, ws = _bwd_outputs(q, workspace, p, (dq, dk, dv))
     lib = _lib.load()
     _lib.check(lib.fa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
@@ -156,10 +167,11 @@ def fa_bwd(q, k, v, o, lse, do, *, scale=None, causal=False, key_lens=None, work
 
 
 def fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, *, mask_block=128, scale=None,
-                       causal=False, key_lens=None, workspace=None, dq=None, dk=None, dv=None):
+                       causal=False, key_lens=None, workspace=None, dq=None, dk=None, dv=None,
+                       dropout_p=0.0, dropout_seed=0, dropout_offset=0):
     """Block-sparse gradients (dQ, dK, dV).  Calls fa_bwd_blocksparse."""
     _same_layout(q, k, v, o, do)
-    p, kl = _problem(q, scale, causal, key_lens)
+    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
     bm, hstride = _mask(block_mask, q)
     dq, dk, dv, ws = _bwd_outputs(q, workspace, p, (dq, dk, dv))
     lib = _lib.load()
@@ -171,12 +183,13 @@ def fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, *, mask_block=128, scale
 
 
 def fa_bwd_ex(q, k, v, o, lse, do, stages, *, block_mask=None, mask_block=128, scale=None,
-              causal=False, key_lens=None, workspace, dq, dk, dv):
+              causal=False, key_lens=None, workspace, dq, dk, dv, dropout_p=0.0, dropout_seed=0,
+              dropout_offset=0):
     """One or more stages of the backward launch sequence (FA_BWD_PRE, _MAIN,
     _DQ bits), writing into caller-provided gradients and workspace.  Calls
     fa_bwd_ex; block_mask None selects the dense path."""
     _same_layout(q, k, v, o, do, dq, dk, dv)
-    p, kl = _problem(q, scale, causal, key_lens)
+    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
     bm, hstride = (None, 0) if block_mask is None else _mask(block_mask, q)
     lib = _lib.load()
     _lib.check(lib.fa_bwd_ex(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),

@@ -14,7 +14,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_bwd_blocksparse", "fa_bwd_ex", "fa_status_string", "fa_last_error",
            "fa_abi_version")
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class FaProblem(ctypes.Structure):
@@ -31,6 +31,9 @@ class FaProblem(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("key_lens", ctypes.c_void_p),
+        ("dropout_p", ctypes.c_float),
+        ("dropout_offset", ctypes.c_uint32),
+        ("dropout_seed", ctypes.c_uint64),
     ]
 
 

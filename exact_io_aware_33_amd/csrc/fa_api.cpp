@@ -52,7 +52,16 @@ fa_status_t check_problem(const fa_problem_t *p) {
     return fail(FA_ERR_INVALID, "stride_n (%lld) smaller than head_dim", (long long)p->stride_n);
   if (p->key_lens && !aligned16(p->key_lens))
     return fail(FA_ERR_INVALID, "key_lens must be 16-byte aligned");
+  if (!std::isfinite(p->dropout_p) || p->dropout_p < 0.f || p->dropout_p >= 1.f)
+    return fail(FA_ERR_INVALID, "dropout_p must be in [0, 1)");
   return FA_OK;
+}
+
+// Dropout threshold t = round-half-even(256 p) clamped to [0, 255]; t = 0
+// keeps every element (no dropout).
+uint32_t drop_threshold(float p) {
+  const double t = std::nearbyint((double)p * 256.0);
+  return (uint32_t)(t < 0.0 ? 0.0 : (t > 255.0 ? 255.0 : t));
 }
 
 fa_status_t check_tensor(const void *ptr, const char *name) {
@@ -84,6 +93,11 @@ fa::AttnParams make_params(const fa_problem_t *p) {
   a.scale_log2 = p->scale * fa::kLog2eHost;
   a.causal = p->causal != 0;
   a.key_lens = p->key_lens;
+  a.drop_thr = drop_threshold(p->dropout_p);
+  a.drop_scale = a.drop_thr ? (float)(256.0 / (256.0 - a.drop_thr)) : 1.f;
+  a.drop_key0 = (uint32_t)(p->dropout_seed & 0xFFFFFFFFu);
+  a.drop_key1 = (uint32_t)(p->dropout_seed >> 32);
+  a.drop_offset = p->dropout_offset;
   return a;
 }
 

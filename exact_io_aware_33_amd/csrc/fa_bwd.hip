@@ -9,6 +9,11 @@
 //     dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic,
 //     dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 // Block-sparse section of the same page: zero mask blocks are skipped here too.
+// With dropout (O = (P o Z) V, Z regenerated from the same Philox counters as
+// the forward's, fa_dropout.hpp) the same derivation with Z held fixed gives
+//     dV = (P o Z)^T dO,  dS = P * (Z o dP - D),  D_i = sum_c dO_ic O_ic
+// (D is unchanged in form: sum_j P_ij Z_ij dP_ij = dO_i . O_i); those
+// instances (DROP) take the generic iteration for every block.
 //
 // Kernels (all on the caller's stream):
 //  1. bwd_pre:   D = rowsum(dO * O) per query row (the only workspace: one
@@ -31,6 +36,7 @@
 #include <type_traits>
 
 #include "fa_device.hpp"
+#include "fa_dropout.hpp"
 #include "fa_internal.hpp"
 
 namespace fa {
@@ -111,7 +117,7 @@ struct BwdCfg {
   static_assert(BQ * CPR % (64 * WAVES) == 0, "query block must split evenly");
 };
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   using C = BwdCfg<T, D>;
   using M = Mma<T>;
@@ -150,6 +156,8 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   const int kw0 = k0 + 32 * wave;  // first key of this wave
   const int key = kw0 + l32;       // this lane's key (column of S)
 
+  // dV accumulates (P o Z / (1 - p))^T dO: the common factor goes here.
+  const float vscale = DROP ? p.drop_scale : 1.f;
   auto store_dkdv = [&](const f32x16 *dkacc, const f32x16 *dvacc) {
     if (key >= N) return;
     T *krow = dK + (int64_t)key * p.sn;
@@ -164,14 +172,15 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
               f32x4{dkacc[nb][4 * i] * p.scale, dkacc[nb][4 * i + 1] * p.scale,
                     dkacc[nb][4 * i + 2] * p.scale, dkacc[nb][4 * i + 3] * p.scale};
           *reinterpret_cast<f32x4 *>(vrow + d0) =
-              f32x4{dvacc[nb][4 * i], dvacc[nb][4 * i + 1], dvacc[nb][4 * i + 2], dvacc[nb][4 * i + 3]};
+              f32x4{dvacc[nb][4 * i] * vscale, dvacc[nb][4 * i + 1] * vscale,
+                    dvacc[nb][4 * i + 2] * vscale, dvacc[nb][4 * i + 3] * vscale};
         } else {
           typedef T t4 __attribute__((ext_vector_type(4)));
           t4 kv4, vv4;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             kv4[j] = (T)(dkacc[nb][4 * i + j] * p.scale);
-            vv4[j] = (T)dvacc[nb][4 * i + j];
+            vv4[j] = (T)(dvacc[nb][4 * i + j] * vscale);
           }
           *reinterpret_cast<t4 *>(krow + d0) = kv4;
           *reinterpret_cast<t4 *>(vrow + d0) = vv4;
@@ -365,7 +374,8 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // order, column = this lane's key).
   auto sdp = [&](const char *ql, f32x16 &S, f32x16 &DP) {
     S = f32x16{};
-    DP = load_negd(ql);
+    if constexpr (DROP) DP = f32x16{};  // dP alone: -D enters after the keep factor
+    else DP = load_negd(ql);
 #pragma unroll
     for (int i = 0; i < NGA; ++i) {
       const int s = i >> 1;
@@ -377,12 +387,18 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - D) with DP = dP - D
   // already, in place; with MASK, invisible (query, key) pairs get
   // P = dS = 0.
+  // With DROP (DP = dP): P o Z / (1 - p) into S and dS = P (Z dP - D) into DP.
   auto softmax_grad = [&](const char *ql, int q0, f32x16 &S, f32x16 &DP, auto masked) {
     const float *ll = reinterpret_cast<const float *>(ql + C::LSE_OFF);
+    const float *dd = reinterpret_cast<const float *>(ql + C::D_OFF);
     const int lim_q = CAUSAL ? key - q0 : -1;  // query row qr visible iff qr >= lim_q
+    uint32_t keepb[4];
+    if constexpr (DROP) keep_bytes_key_col(keepb, p, bh, q0, key, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ll + 8 * i + 4 * h);
+      f32x4 nd4;
+      if constexpr (DROP) nd4 = *reinterpret_cast<const f32x4 *>(dd + 8 * i + 4 * h);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * i + j;
@@ -390,8 +406,14 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
         if constexpr (decltype(masked)::value) {
           if (!(key < kv_len && reg_row(r, h) >= lim_q)) pv = 0.f;
         }
-        S[r] = pv;
-        DP[r] = pv * DP[r];
+        if constexpr (DROP) {
+          const bool kp = kept(keepb, r, p.drop_thr);
+          S[r] = kp ? pv : 0.f;
+          DP[r] = pv * fmaf(kp ? p.drop_scale : 0.f, DP[r], nd4[j]);
+        } else {
+          S[r] = pv;
+          DP[r] = pv * DP[r];
+        }
       }
     }
   };
@@ -517,7 +539,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // the end of this key tile), or every block when the key tile crosses the
   // padding length.
   int n_masked = 0;
-  if (k0 + C::BKC > kv_len) {
+  if (DROP || k0 + C::BKC > kv_len) {
     n_masked = nq;
   } else if (CAUSAL) {
     while (n_masked < nq && qblock_start(n_masked) < k0 + C::BKC) ++n_masked;
@@ -537,19 +559,21 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   }
   // Steady blocks in trips of NSLOT (so the slots are compile-time
   // constants); the trip must start at a block index that is 0 mod NSLOT.
-  for (; i < nq - 1 && (i & (C::NSLOT - 1)) != 0; ++i) {
-    iter_any(i, SA, DA, SB, DB);
-    swap_ab();
-  }
-  using s0 = std::integral_constant<int, 0>;
-  using s1 = std::integral_constant<int, 1>;
-  using s2 = std::integral_constant<int, 2>;
-  using s3 = std::integral_constant<int, 3>;
-  for (; i + C::NSLOT < nq; i += C::NSLOT) {
-    iter_steady(i, s0{}, SA, DA, SB, DB);
-    iter_steady(i + 1, s1{}, SB, DB, SA, DA);
-    iter_steady(i + 2, s2{}, SA, DA, SB, DB);
-    iter_steady(i + 3, s3{}, SB, DB, SA, DA);
+  if constexpr (!DROP) {
+    for (; i < nq - 1 && (i & (C::NSLOT - 1)) != 0; ++i) {
+      iter_any(i, SA, DA, SB, DB);
+      swap_ab();
+    }
+    using s0 = std::integral_constant<int, 0>;
+    using s1 = std::integral_constant<int, 1>;
+    using s2 = std::integral_constant<int, 2>;
+    using s3 = std::integral_constant<int, 3>;
+    for (; i + C::NSLOT < nq; i += C::NSLOT) {
+      iter_steady(i, s0{}, SA, DA, SB, DB);
+      iter_steady(i + 1, s1{}, SB, DB, SA, DA);
+      iter_steady(i + 2, s2{}, SA, DA, SB, DB);
+      iter_steady(i + 3, s3{}, SB, DB, SA, DA);
+    }
   }
   for (; i < nq; ++i) {
     iter_any(i, SA, DA, SB, DB);
@@ -587,7 +611,7 @@ struct DqCfg {
   static_assert(BC * CPR % (64 * WAVES) == 0, "tile must split evenly");
 };
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 // d = 128: at most 256 VGPRs, so that two waves share each SIMD
 __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnParams p) {
   using C = DqCfg<T, D>;
@@ -782,7 +806,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
 #pragma unroll
     for (int i = 0; i < NGA; ++i) {
       const int s = i >> 1;
-      if (i & 1) DP = M::mma32(kvfrag(kl, i), gf[s], s == 0 ? negd : DP);
+      if (i & 1) DP = M::mma32(kvfrag(kl, i), gf[s], s == 0 ? (DROP ? f32x16{} : negd) : DP);
       else S = M::mma32(kvfrag(kl, i), qf[s], S);
       FA_FENCE();  // bounds the operand reads in flight (register pressure)
     }
@@ -792,6 +816,11 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   auto grad_row = [&](f32x16 &S, f32x16 &DP, int r) {
     const float pv = fast_exp2(fmaf(S[r], c2, -lse2));
     DP[r] = pv * DP[r];
+  };
+  // With DROP (DP = dP^T): dS^T = P (Z dP - D).
+  auto grad_row_drop = [&](f32x16 &S, f32x16 &DP, int r, const uint32_t (&keepb)[4]) {
+    const float pv = fast_exp2(fmaf(S[r], c2, -lse2));
+    DP[r] = pv * fmaf(kept(keepb, r, p.drop_thr) ? p.drop_scale : 0.f, DP[r], negdl);
   };
   // dQ^T += K^T dS^T  (rows = d, column = this lane's query)
   auto dqacc = [&](const char *kl, const f32x16 &DS) {
@@ -815,9 +844,12 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
     fetch(j + C::AHEAD);
     const char *kl = slot(j), *kn = slot(j + 1);
     const int lim_o = (CAUSAL ? min(kv_len, qi + 1) : kv_len) - tile_start(j);
+    uint32_t keepb[4];
+    if constexpr (DROP) keep_bytes_query_col(keepb, p, bh, qi, tile_start(j), lane);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      grad_row(SX, DX, r);
+      if constexpr (DROP) grad_row_drop(SX, DX, r, keepb);
+      else grad_row(SX, DX, r);
       if (!(reg_row(r, 0) + 4 * h < lim_o)) DX[r] = 0.f;  // key kv0 + row invisible
     }
     sdp(kn, SY, DY);
@@ -896,12 +928,14 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   using s1 = std::integral_constant<int, 1>;
   using s2 = std::integral_constant<int, 2>;
   using s3 = std::integral_constant<int, 3>;
-  const int j_steady = min(n_full, ntiles - 1);  // tile j unmasked, j+1 exists
-  for (; j + C::NSLOT <= j_steady; j += C::NSLOT) {
-    iter_steady(j, s0{}, SA, DA, SB, DB);
-    iter_steady(j + 1, s1{}, SB, DB, SA, DA);
-    iter_steady(j + 2, s2{}, SA, DA, SB, DB);
-    iter_steady(j + 3, s3{}, SB, DB, SA, DA);
+  if constexpr (!DROP) {
+    const int j_steady = min(n_full, ntiles - 1);  // tile j unmasked, j+1 exists
+    for (; j + C::NSLOT <= j_steady; j += C::NSLOT) {
+      iter_steady(j, s0{}, SA, DA, SB, DB);
+      iter_steady(j + 1, s1{}, SB, DB, SA, DA);
+      iter_steady(j + 2, s2{}, SA, DA, SB, DB);
+      iter_steady(j + 3, s3{}, SB, DB, SA, DA);
+    }
   }
   for (; j < ntiles; ++j) {
     iter_any(j, SA, DA, SB, DB);
@@ -932,30 +966,30 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_main_t(const AttnParams &p, hipStream_t s) {
   using C = BwdCfg<T, D>;
   const int64_t nkt = (p.N + C::BKC - 1) / C::BKC;
   const int64_t grid = (int64_t)p.B * p.H * nkt;
   AttnParams a = p;
   void *args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_main_kernel<T, D, CAUSAL, SPARSE>),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_main_kernel<T, D, CAUSAL, SPARSE, DROP>),
                          dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_dq_t(const AttnParams &p, hipStream_t s) {
   using C = DqCfg<T, D>;
   const int64_t nqt = (p.N + C::BR - 1) / C::BR;
   const int64_t grid = (int64_t)p.B * p.H * nqt;
   AttnParams a = p;
   void *args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel<T, D, CAUSAL, SPARSE>),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP>),
                          dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
-template <typename T, int D>
-static hipError_t launch_bwd_d(const AttnParams &p, bool sparse, unsigned stages, hipStream_t s) {
+template <typename T, int D, bool DROP>
+static hipError_t launch_bwd_dd(const AttnParams &p, bool sparse, unsigned stages, hipStream_t s) {
   AttnParams a = p;
   void *args[] = {&a};
   const int64_t rows = (int64_t)p.B * p.H * p.N;
@@ -967,18 +1001,24 @@ static hipError_t launch_bwd_d(const AttnParams &p, bool sparse, unsigned stages
   }
   if (stages & FA_BWD_MAIN) {
     if (sparse)
-      e = p.causal ? launch_main_t<T, D, true, true>(p, s) : launch_main_t<T, D, false, true>(p, s);
+      e = p.causal ? launch_main_t<T, D, true, true, DROP>(p, s) : launch_main_t<T, D, false, true, DROP>(p, s);
     else
-      e = p.causal ? launch_main_t<T, D, true, false>(p, s) : launch_main_t<T, D, false, false>(p, s);
+      e = p.causal ? launch_main_t<T, D, true, false, DROP>(p, s) : launch_main_t<T, D, false, false, DROP>(p, s);
     if (e != hipSuccess) return e;
   }
   if (stages & FA_BWD_DQ) {
     if (sparse)
-      e = p.causal ? launch_dq_t<T, D, true, true>(p, s) : launch_dq_t<T, D, false, true>(p, s);
+      e = p.causal ? launch_dq_t<T, D, true, true, DROP>(p, s) : launch_dq_t<T, D, false, true, DROP>(p, s);
     else
-      e = p.causal ? launch_dq_t<T, D, true, false>(p, s) : launch_dq_t<T, D, false, false>(p, s);
+      e = p.causal ? launch_dq_t<T, D, true, false, DROP>(p, s) : launch_dq_t<T, D, false, false, DROP>(p, s);
   }
   return e;
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_d(const AttnParams &p, bool sparse, unsigned stages, hipStream_t s) {
+  return p.drop_thr ? launch_bwd_dd<T, D, true>(p, sparse, stages, s)
+                    : launch_bwd_dd<T, D, false>(p, sparse, stages, s);
 }
 
 template <typename T>

@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "fa_device.hpp"
+#include "fa_dropout.hpp"
 #include "fa_internal.hpp"
 
 namespace fa {
@@ -94,10 +95,14 @@ constexpr float kMaxSlack = 8.0f;
 // the issue order.
 #define FA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+// DROP: dropout on P (keep decisions regenerated per tile, see fa_dropout.hpp);
+// every tile then takes the generic iteration.
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 // d = 64: registers bounded for three waves per SIMD (the few spills this
-// costs sit outside the tile loops).
-__global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? 3 : 1)) fwd_kernel(AttnParams p) {
+// costs sit outside the tile loops); two with dropout, whose generator needs
+// the registers.
+__global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP ? 2 : 3) : 1))
+    fwd_kernel(AttnParams p) {
   using C = FwdCfg<T, D, SPARSE>;
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -377,16 +382,24 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? 3 : 1
       }
     }
   };
-  // step 4: O_i^T += V_j^T P^T for P in `P`, plus the row sums.
-  auto pv = [&](const char *vl, const f32x16 (&P)[NBLK]) {
+  // step 4: O_i^T += V_j^T P^T for P in `P` (the tile at key kv0), plus the
+  // row sums.  With dropout the row sums take P and the product P o Z (Z's
+  // common factor 1 / (1 - p) is applied in the epilogue).
+  const uint32_t drop_add = keep_pair_add(p.drop_thr);
+  auto pv = [&](const char *vl, const f32x16 (&P)[NBLK], int kv0) {
+    uint32_t keepb[QB][4];
 #pragma unroll
     for (int k = 0; k < NS1; ++k) {
       const int sb = k / C::PSTEPS, t = k - sb * C::PSTEPS;
       frag pb[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (DROP) {
+          if (t == 0) keep_bytes_query_col(keepb[qb], p, bh, qw0 + 32 * qb + l32, kv0 + 32 * sb, lane);
+        }
         pb[qb] = pack_frag<T>(P[qb * NSB + sb], t * KPL);
         rowsum(qb, pb[qb]);
+        if constexpr (DROP) pb[qb] = drop_frag<T>(pb[qb], keepb[qb], t * KPL, p.drop_thr, drop_add);
       }
 #pragma unroll
       for (int nb = 0; nb < C::NOB; ++nb) {
@@ -408,7 +421,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? 3 : 1
   auto iter_any = [&](int j, auto first, f32x16 (&X)[NBLK], f32x16 (&Y)[NBLK]) {
     fetch(true, stv, vslot(j), tile_start(j));
     fetch(false, stk, kslot(j), tile_start(min(j + 2, ntiles - 1)));
-    if constexpr (!decltype(first)::value) pv(vslot(j - 1), Y);
+    if constexpr (!decltype(first)::value) pv(vslot(j - 1), Y, tile_start(j - 1));
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
@@ -537,33 +550,35 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? 3 : 1
     iter_any(j++, ftrue{}, SB, SA);
     rotate();
   }
-  const int j_steady = min(n_full, ntiles) - 1;  // tiles j and j+1 unmasked
-  // Two iterations per trip restore the roles at the loop back edge, so the
-  // steady loop needs no register copies.
-  using odd = std::integral_constant<int, 1>;
-  using even = std::integral_constant<int, 0>;
-  for (; j + 1 < j_steady; j += 2) {
-    iter_steady(j, odd{}, SB, SA);
-    iter_steady(j + 1, even{}, SA, SB);
-  }
-  if (j < j_steady) {
-    iter_steady(j++, odd{}, SB, SA);
-    rotate();
+  if constexpr (!DROP) {
+    const int j_steady = min(n_full, ntiles) - 1;  // tiles j and j+1 unmasked
+    // Two iterations per trip restore the roles at the loop back edge, so the
+    // steady loop needs no register copies.
+    using odd = std::integral_constant<int, 1>;
+    using even = std::integral_constant<int, 0>;
+    for (; j + 1 < j_steady; j += 2) {
+      iter_steady(j, odd{}, SB, SA);
+      iter_steady(j + 1, even{}, SA, SB);
+    }
+    if (j < j_steady) {
+      iter_steady(j++, odd{}, SB, SA);
+      rotate();
+    }
   }
   for (; j < ntiles; ++j) {
     iter_any(j, ffalse{}, SB, SA);
     rotate();
   }
-  if (ntiles > 0) pv(vslot(ntiles - 1), SA);
+  if (ntiles > 0) pv(vslot(ntiles - 1), SA, tile_start(ntiles - 1));
 #undef EL
 
-  // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = O / l (times 1 / (1 - p) with dropout), LSE = (m + log2 l) ln 2
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = qw0 + 32 * qb + l32;
     const float l_half = (lpart[qb][0] + lpart[qb][1]) + (lpart[qb][2] + lpart[qb][3]);
     const float l_tot = l_half + xor32(l_half);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) / l_tot : 0.f;
     if (qi < N) {
       T *orow = O + (int64_t)qi * p.sn;
 #pragma unroll
@@ -589,21 +604,27 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? 3 : 1
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_fwd_t(const AttnParams &p, hipStream_t s) {
   using C = FwdCfg<T, D, SPARSE>;
   const int64_t nqt = (p.N + C::BR - 1) / C::BR;
   const int64_t grid = (int64_t)p.B * p.H * nqt;
   AttnParams a = p;
   void *args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE>),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE, DROP>),
                          dim3((unsigned)grid), dim3(C::NTHR), args, 0, s);
+}
+
+template <typename T, int D, bool DROP>
+static hipError_t launch_fwd_dd(const AttnParams &p, bool sparse, hipStream_t s) {
+  if (sparse)
+    return p.causal ? launch_fwd_t<T, D, true, true, DROP>(p, s) : launch_fwd_t<T, D, false, true, DROP>(p, s);
+  return p.causal ? launch_fwd_t<T, D, true, false, DROP>(p, s) : launch_fwd_t<T, D, false, false, DROP>(p, s);
 }
 
 template <typename T, int D>
 static hipError_t launch_fwd_d(const AttnParams &p, bool sparse, hipStream_t s) {
-  if (sparse) return p.causal ? launch_fwd_t<T, D, true, true>(p, s) : launch_fwd_t<T, D, false, true>(p, s);
-  return p.causal ? launch_fwd_t<T, D, true, false>(p, s) : launch_fwd_t<T, D, false, false>(p, s);
+  return p.drop_thr ? launch_fwd_dd<T, D, true>(p, sparse, s) : launch_fwd_dd<T, D, false>(p, sparse, s);
 }
 
 template <typename T>

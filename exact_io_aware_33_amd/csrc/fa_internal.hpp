@@ -34,6 +34,11 @@ struct AttnParams {
   int32_t mb;                // block size (multiple of 128)
   int32_t nblk;              // N / mb
   int64_t mask_hstride;      // bytes between heads' masks (0 = shared)
+  // dropout (Philox4x32-10 keep decisions); drop_thr == 0: none
+  uint32_t drop_thr;         // t: an element whose decision byte is < t is dropped
+  float drop_scale;          // 256 / (256 - t), the factor of kept elements
+  uint32_t drop_key0, drop_key1;  // Philox key (seed low, high word)
+  uint32_t drop_offset;      // fourth counter word
 };
 
 // Launchers (defined in fa_fwd.hip / fa_bwd.hip).  They assume validated

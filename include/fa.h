@@ -19,6 +19,22 @@
  *   block mask  : M[i / mb][j / mb] != 0        (the *_blocksparse entry points)
  * A query row with no visible key gets O = 0, LSE = -inf and zero gradients.
  *
+ * Dropout (same page, "Key ideas", kernel-fusion bullet: dropout is one of
+ * the steps fused into the attention kernel; the page fixes no generator).
+ * With dropout_p > 0 the forward computes O = (P o Z) V, where Z_ij is 0
+ * (dropped) or 1 / (1 - t/256) (kept) and t = round-half-even(256 p),
+ * clamped to [0, 255], computed in double from the float field.  The keep
+ * decisions come from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+ * random numbers: as easy as 1, 2, 3", SC'11) with
+ *     key     = (dropout_seed mod 2^32, dropout_seed div 2^32),
+ *     counter = (i / 4, j / 4, b * H + h, dropout_offset):
+ * output word w of that call decides query 4 (i / 4) + w, its byte k
+ * (bits 8k .. 8k+7) key 4 (j / 4) + k, and the element is kept iff that
+ * byte >= t.  The decisions are a function of (seed, offset, b, h, i, j)
+ * only: the backward pass regenerates them instead of storing Z, and its
+ * gradients are those of <dO, (P o Z) V> with Z held fixed.  LSE is the
+ * statistics of P, unaffected by dropout.
+ *
  * Saved statistics: the forward pass writes LSE_i = m_i + ln(l_i), the natural
  * log-sum-exp of the scaled, masked score row i (the summary page keeps (l, m)
  * for the backward pass; LSE carries the same information, P = exp(S - LSE)).
@@ -64,7 +80,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum fa_dtype {
   FA_DTYPE_F32 = 0,   /* IEEE float32 storage, float32 arithmetic            */
@@ -75,8 +91,9 @@ typedef enum fa_dtype {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID = 1,      /* bad argument: NULL pointer, size <= 0, non-finite
-                              or negative scale, workspace too small, block size
-                              that does not divide N, misaligned pointer       */
+                              or negative scale, dropout_p outside [0, 1),
+                              workspace too small, block size that does not
+                              divide N, misaligned pointer                    */
   FA_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim / dtype pair,
                               block size not a multiple of 128, sizes over the
                               32-bit index range                              */
@@ -98,6 +115,11 @@ typedef struct fa_problem {
   const int32_t *key_lens;  /* device int32 [B] or NULL (no padding): keys
                                j >= key_lens[b] are masked for every query and
                                head of batch b; clamped to [0, N] on device    */
+  float dropout_p;          /* probability of dropping an element of P, in
+                               [0, 1); 0 = no dropout (then the two fields
+                               below are ignored)                             */
+  uint32_t dropout_offset;  /* fourth Philox counter word (e.g. a step count) */
+  uint64_t dropout_seed;    /* Philox key                                     */
 } fa_problem_t;
 
 /* Forward pass (summary page, "Incremental softmax tracking", steps 1-4).
@@ -140,7 +162,8 @@ size_t fa_bwd_workspace_bytes(const fa_problem_t *p);
  *   workspace  : device scratch of at least fa_bwd_workspace_bytes(p) bytes,
  *                owned by the caller, contents on entry ignored; it must not
  *                be shared with a concurrently running call.
- * The mask fields of p must equal those used for the forward pass. */
+ * The mask and dropout fields of p must equal those used for the forward
+ * pass. */
 fa_status_t fa_bwd(const fa_problem_t *p, const void *q, const void *k,
                    const void *v, const void *o, const float *lse,
                    const void *dout, void *dq, void *dk, void *dv,

@@ -53,7 +53,7 @@ def test_exports_match_header(lib):
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == _lib.ABI_VERSION == 2
 
 
 def test_status_strings(lib):
@@ -69,6 +69,8 @@ def test_status_strings(lib):
     ("scale", -0.5, INVALID), ("stride_n", 60, INVALID), ("stride_n", 36, INVALID),
     ("stride_h", -64, INVALID), ("key_lens", 0x10004, INVALID),
     ("seqlen", 1 << 30, UNSUPPORTED),
+    ("dropout_p", -0.1, INVALID), ("dropout_p", 1.0, INVALID), ("dropout_p", 1.5, INVALID),
+    ("dropout_p", float("nan"), INVALID), ("dropout_p", float("inf"), INVALID),
 ])
 def test_problem_rejected_before_any_hip_call(lib, field, value, status):
     p = prob(**{field: value})
@@ -145,3 +147,22 @@ def test_python_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libfa.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_problem_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of fa_problem_t has the C compiler's field offsets."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in _lib.FaProblem._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"fa.h\"\nint main(void) {\n"
+                   + "".join(f'  printf("%zu\\n", offsetof(fa_problem_t, {f}));\n' for f in fields)
+                   + '  printf("%zu\\n", sizeof(fa_problem_t));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [getattr(_lib.FaProblem, f).offset for f in fields] + [ctypes.sizeof(_lib.FaProblem)]
+    assert got == want
