@@ -16,6 +16,10 @@ through fa_bwd_ex, all on torch's current stream.  Prints ONE JSON line on stdou
              committed rocprofv3 counter summary when it was taken on the
              current kernel sources, else null.
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
+
+--dropout P runs the same step with fused dropout (probability P, Philox
+counter offset = step index, as a training loop would advance it); FLOPs are
+counted as without dropout (the keep decisions are not matrix work).
 """
 from __future__ import annotations
 
@@ -94,7 +98,7 @@ def traffic_from_profile(workload: str, kernel: str):
     return k["fetch_bytes"] + k["write_bytes"]
 
 
-def cpu_baseline(w, inputs, budget_heads=1):
+def cpu_baseline(w, inputs, budget_heads=1, dropout=None):
     """The oracle as it stands, timed on this host on one (batch, head) of the
     workload (full N, forward + backward)."""
     import numpy as np
@@ -112,13 +116,14 @@ def cpu_baseline(w, inputs, budget_heads=1):
     bm = None if inputs["block_mask"] is None else inputs["block_mask"].numpy()
     t0 = time.perf_counter()
     oracle.backward(q, k, v, do, w.scale, causal=w.causal, key_lens=lens, block_mask=bm,
-                    mb=w.mb or 128)
+                    mb=w.mb or 128, dropout=dropout)
     dt = time.perf_counter() - t0
     flops_fwd = 4.0 * budget_heads * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
     return {"value": round(3.5 * flops_fwd / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads, "kind": "oracle",
             "sample": f"1 batch x {budget_heads} head(s) of {w.name} (N={w.N}, d={w.d}), "
-                      f"fp64 numpy two-pass forward + analytic backward, {dt:.1f} s; "
+                      f"fp64 numpy two-pass forward + analytic backward"
+                      f"{'' if dropout is None else f' with dropout p={dropout[0]}'}, {dt:.1f} s; "
                       f"host os.cpu_count()={os.cpu_count()}"}
 
 
@@ -129,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="fused dropout probability (0 = none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -175,35 +182,38 @@ def main():
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     common = dict(scale=w.scale, causal=w.causal, key_lens=kl)
+    drop_seed = 0x5EED
 
-    def fwd():
+    def fwd(i):
+        dr = dict(dropout_p=args.dropout, dropout_seed=drop_seed, dropout_offset=i)
         if bm is None:
-            fa_fwd(q, k, v, out=o, lse=lse, **common)
+            fa_fwd(q, k, v, out=o, lse=lse, **common, **dr)
         else:
-            fa_fwd_blocksparse(q, k, v, bm, mask_block=w.mb, out=o, lse=lse, **common)
+            fa_fwd_blocksparse(q, k, v, bm, mask_block=w.mb, out=o, lse=lse, **common, **dr)
 
-    def bwd(stage):
+    def bwd(stage, i):
+        dr = dict(dropout_p=args.dropout, dropout_seed=drop_seed, dropout_offset=i)
         fa_bwd_ex(q, k, v, o, lse, do, stage, block_mask=bm, mask_block=w.mb or 128,
-                  workspace=ws, dq=dq, dk=dk, dv=dv, **common)
+                  workspace=ws, dq=dq, dk=dk, dv=dv, **common, **dr)
 
-    def step(ev=None):
+    def step(i, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fwd()
+        fwd(i)
         if ev is not None:
             ev[1].record(stream)
-        bwd(FA_BWD_PRE)
+        bwd(FA_BWD_PRE, i)
         if ev is not None:
             ev[2].record(stream)
-        bwd(FA_BWD_MAIN)
+        bwd(FA_BWD_MAIN, i)
         if ev is not None:
             ev[3].record(stream)
-        bwd(FA_BWD_DQ)
+        bwd(FA_BWD_DQ, i)
         if ev is not None:
             ev[4].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
@@ -211,7 +221,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(args.warmup + i, events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -237,7 +247,8 @@ def main():
     dur_ms, alg_flops = kernels[name]
     achieved = alg_flops / (dur_ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
-    traffic = traffic_from_profile(w.name, name)
+    label = w.name if args.dropout == 0.0 else f"{w.name}_dropout{args.dropout:g}"
+    traffic = traffic_from_profile(label, name)
 
     out = {
         "metric": "attention TFLOP/s fwd & fwd+bwd, N=1K-16K d=64 bf16; % of MFMA peak",
@@ -253,7 +264,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "mask_block": w.mb, "key_padding": w.lens is not None},
+                   "causal": w.causal, "mask_block": w.mb, "key_padding": w.lens is not None,
+                   "dropout": args.dropout},
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
         "bwd_tflops": round(2.5 * f_fwd / ((pre_ms + main_ms + dq_ms) * 1e-3) / 1e12, 3),
         "mfma_peak_frac_step": round(value / peak, 4),
@@ -266,7 +278,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (cpu_baseline)...")
-        out["cpu_baseline"] = cpu_baseline(w, inputs)
+        out["cpu_baseline"] = cpu_baseline(
+            w, inputs, dropout=None if args.dropout == 0.0 else (args.dropout, drop_seed, 0))
         log(f"[bench] cpu_baseline done: {out['cpu_baseline']['value']} TFLOP/s")
     print(json.dumps(out), flush=True)
 
