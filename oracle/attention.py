@@ -18,6 +18,10 @@ What is computed, and where the pages define it
   block-sparse section of that page defines the block mask M over row and
   column blocks.  Readings (scale applied before masking, causal j <= i,
   key padding j < len_b, block (i // mb, j // mb)) are listed in DESIGN.md.
+  With N_q queries and N_k keys (N_q != N_k: cross-attention, decoding) the
+  causal rule is aligned at the bottom right, j <= i + (N_k - N_q): the
+  queries are the last N_q positions of the key sequence (the pages define
+  causal masking only by name).
 * The gradients are not printed on the pages; they are the analytic
   derivatives of the definition above for the loss <dO, O>:
       dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
@@ -56,17 +60,20 @@ def _block_mask_for_head(block_mask, h):
     return bm
 
 
-def allowed_mask(rows, N, *, causal=False, key_len=None, block_mask=None, mb=128):
-    """Boolean [len(rows), N]: True where query ``rows[r]`` may see key j.
+def allowed_mask(rows, N, *, causal=False, key_len=None, block_mask=None, mb=128,
+                 n_queries=None):
+    """Boolean [len(rows), N]: True where query ``rows[r]`` may see key j < N.
 
-    The allowed set is the AND of every active mask:
-    causal (j <= i), key padding (j < key_len) and block (M[i//mb, j//mb] != 0).
+    The allowed set is the AND of every active mask: causal
+    (j <= i + N - n_queries; n_queries defaults to N, giving j <= i), key
+    padding (j < key_len) and block (M[i//mb, j//mb] != 0).
     """
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.arange(N, dtype=np.int64)
     a = np.ones((rows.size, N), dtype=bool)
     if causal:
-        a &= cols[None, :] <= rows[:, None]
+        shift = 0 if n_queries is None else N - int(n_queries)
+        a &= cols[None, :] <= rows[:, None] + shift
     if key_len is not None:
         a &= cols[None, :] < int(key_len)
     if block_mask is not None:
@@ -100,8 +107,9 @@ def forward_rows(q, k, v, scale, rows, *, causal=False, key_len=None,
                  block_mask=None, mb=128, dropout=None, bh=0):
     """O and LSE of one (batch, head) for the query indices ``rows`` only.
 
-    q: [N, d] (only ``rows`` are read), k, v: [N, d].  Returns (o [R, d],
-    lse [R]).  Used for sampled parity at sizes where every row is too many.
+    q: [N_q, d] (only ``rows`` are read), k, v: [N_k, d].  Returns
+    (o [R, d], lse [R]).  Used for sampled parity at sizes where every row is
+    too many.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -110,7 +118,7 @@ def forward_rows(q, k, v, scale, rows, *, causal=False, key_len=None,
     rows = np.asarray(rows, dtype=np.int64)
     s = float(scale) * (q[rows] @ k.T)
     a = allowed_mask(rows, N, causal=causal, key_len=key_len,
-                     block_mask=block_mask, mb=mb)
+                     block_mask=block_mask, mb=mb, n_queries=q.shape[0])
     s = np.where(a, s, -np.inf)
     m, l, valid, e = _row_softmax_stats(s)
     p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
@@ -153,7 +161,7 @@ def forward(q, k, v, scale, *, causal=False, key_lens=None, block_mask=None,
 
 
 def probabilities(q, k, scale, *, causal=False, key_len=None, block_mask=None, mb=128):
-    """P = softmax of the scaled, masked score matrix of one (batch, head): [N, N].
+    """P = softmax of the scaled, masked score matrix of one (batch, head): [N_q, N_k].
 
     A row with no visible key is all zeros.  Only for small N (tests).
     """
@@ -163,7 +171,7 @@ def probabilities(q, k, scale, *, causal=False, key_len=None, block_mask=None, m
     rows = np.arange(q.shape[0])
     s = float(scale) * (q @ k.T)
     s = np.where(allowed_mask(rows, N, causal=causal, key_len=key_len,
-                              block_mask=block_mask, mb=mb), s, -np.inf)
+                              block_mask=block_mask, mb=mb, n_queries=q.shape[0]), s, -np.inf)
     m, l, valid, e = _row_softmax_stats(s)
     return np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
 
@@ -177,10 +185,11 @@ def backward(q, k, v, do, scale, *, causal=False, key_lens=None, block_mask=None
     exact arithmetic; the GPU computes the latter.
     """
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     dq = np.zeros_like(q, dtype=np.float64)
     dk = np.zeros_like(k, dtype=np.float64)
     dv = np.zeros_like(v, dtype=np.float64)
-    o = np.zeros((B, H, N, d), np.float64)
+    o = np.zeros((B, H, N, v.shape[-1]), np.float64)
     lse = np.zeros((B, H, N), np.float64)
     D_p = np.zeros((B, H, N), np.float64)
     D_o = np.zeros((B, H, N), np.float64)
@@ -192,12 +201,12 @@ def backward(q, k, v, do, scale, *, causal=False, key_lens=None, block_mask=None
             for r0 in range(0, N, chunk):
                 rows = np.arange(r0, min(N, r0 + chunk))
                 s = float(scale) * (qb[rows] @ kb.T)
-                a = allowed_mask(rows, N, causal=causal, key_len=lens[b],
-                                 block_mask=bm, mb=mb)
+                a = allowed_mask(rows, Nk, causal=causal, key_len=lens[b],
+                                 block_mask=bm, mb=mb, n_queries=N)
                 s = np.where(a, s, -np.inf)
                 m, l, valid, e = _row_softmax_stats(s)
                 p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
-                z = _z(b * H + h, rows, np.arange(N), dropout)
+                z = _z(b * H + h, rows, np.arange(Nk), dropout)
                 pz = p if z is None else p * z
                 oc = pz @ vb
                 dpc = dob[rows] @ vb.T
@@ -230,15 +239,16 @@ def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=N
     selected columns.
     """
     q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
-    N = k.shape[0]
+    Nq, N = q.shape[0], k.shape[0]
+    mk = dict(causal=causal, key_len=key_len, block_mask=block_mask, mb=mb, n_queries=Nq)
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
-    lse_all = np.empty(N)
-    D_all = np.empty(N)
-    for r0 in range(0, N, chunk):
-        rr = np.arange(r0, min(N, r0 + chunk))
+    lse_all = np.empty(Nq)
+    D_all = np.empty(Nq)
+    for r0 in range(0, Nq, chunk):
+        rr = np.arange(r0, min(Nq, r0 + chunk))
         s = float(scale) * (q[rr] @ k.T)
-        a = allowed_mask(rr, N, causal=causal, key_len=key_len, block_mask=block_mask, mb=mb)
+        a = allowed_mask(rr, N, **mk)
         s = np.where(a, s, -np.inf)
         m, l, valid, e = _row_softmax_stats(s)
         p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
@@ -250,7 +260,7 @@ def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=N
         D_all[rr] = np.sum(p * dp, axis=1)
     # selected rows: O, LSE, dQ
     s = float(scale) * (q[rows] @ k.T)
-    a = allowed_mask(rows, N, causal=causal, key_len=key_len, block_mask=block_mask, mb=mb)
+    a = allowed_mask(rows, N, **mk)
     s = np.where(a, s, -np.inf)
     lr = lse_all[rows]
     fin = np.isfinite(lr)
@@ -263,10 +273,10 @@ def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=N
     # selected columns: dK, dV
     dk_cols = np.zeros((cols.size, q.shape[1]))
     dv_cols = np.zeros((cols.size, v.shape[1]))
-    for r0 in range(0, N, chunk):
-        rr = np.arange(r0, min(N, r0 + chunk))
+    for r0 in range(0, Nq, chunk):
+        rr = np.arange(r0, min(Nq, r0 + chunk))
         s = float(scale) * (q[rr] @ k[cols].T)
-        a = allowed_mask(rr, N, causal=causal, key_len=key_len, block_mask=block_mask, mb=mb)[:, cols]
+        a = allowed_mask(rr, N, **mk)[:, cols]
         s = np.where(a, s, -np.inf)
         lc = lse_all[rr]
         fin = np.isfinite(lc)

@@ -21,6 +21,7 @@ import oracle.attention
 import oracle.dropout
 from tests import test_oracle as pins
 from tests import test_oracle_dropout as drop_pins
+from tests import test_oracle_rect as rect_pins
 
 _ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(_ORACLE, "attention.py")
@@ -71,6 +72,20 @@ DROP_MUTANTS = [
     ("keep on byte > t", DROP_SRC, "return byte >= np.uint64(t)", "return byte > np.uint64(t)"),
     ("seed high word dropped", DROP_SRC, "seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)",
      "seed & 0xFFFFFFFF, 0)"),
+]
+
+
+# Mistakes in the N_q != N_k generalisation, caught by the rectangular pins.
+RECT_MUTANTS = [
+    ("causal aligned top-left", "shift = 0 if n_queries is None else N - int(n_queries)", "shift = 0"),
+    ("causal offset with the wrong sign", "shift = 0 if n_queries is None else N - int(n_queries)",
+     "shift = 0 if n_queries is None else int(n_queries) - N"),
+    ("backward mask without the query count", "a = allowed_mask(rows, Nk, causal=causal, key_len=lens[b],\n"
+     "                                 block_mask=bm, mb=mb, n_queries=N)",
+     "a = allowed_mask(rows, Nk, causal=causal, key_len=lens[b],\n"
+     "                                 block_mask=bm, mb=mb)"),
+    ("sampled D pass over key count", "    for r0 in range(0, Nq, chunk):\n        rr = np.arange(r0, min(Nq, r0 + chunk))\n        s = float(scale) * (q[rr] @ k.T)",
+     "    for r0 in range(0, N, chunk):\n        rr = np.arange(r0, min(N, r0 + chunk))\n        s = float(scale) * (q[rr] @ k.T)"),
 ]
 
 
@@ -147,9 +162,17 @@ def test_dropout_pins_kill_mutant(monkeypatch, label, path, old, new):
     assert _first_failing_pin(drop_pins) is not None, f"no dropout pin catches the mutant: {label}"
 
 
+@pytest.mark.parametrize("label,old,new", RECT_MUTANTS, ids=[m[0] for m in RECT_MUTANTS])
+def test_rect_pins_kill_mutant(monkeypatch, label, old, new):
+    mut = _load_mutant(old, new)
+    for attr in _ATTN:
+        monkeypatch.setattr(oracle, attr, getattr(mut, attr))
+    assert _first_failing_pin(rect_pins) is not None, f"no rectangular pin catches the mutant: {label}"
+
+
 def test_pins_pass_on_the_real_oracle():
     """Sanity: the same harness finds no failing pin on the unmutated oracle."""
-    for p in (pins, drop_pins):
+    for p in (pins, drop_pins, rect_pins):
         for name, fn, kwargs in _pin_calls(p):
             try:
                 fn(**kwargs)
