@@ -57,31 +57,47 @@ def kernel_source_hash() -> str:
 
 
 def visible_pairs(w, key_lens=None, block_mask=None) -> int:
-    """Number of (query, key) pairs no mask removes, summed over batch and heads."""
-    N = w.N
+    """Number of (query, key) pairs no mask removes, summed over batch and heads
+    (causal: key j visible to query i iff j <= i + N_k - N_q)."""
+    import numpy as np
+    Nq, Nk = w.N, w.Nk
+    cs = Nk - Nq if w.causal else None
     if w.mb is not None:
-        import numpy as np
-        bmk = np.asarray(block_mask).astype(bool)
-        if w.causal:
-            below = np.tril(bmk, -1).sum() * w.mb * w.mb
-            diag = np.diag(bmk).sum() * (w.mb * (w.mb + 1) // 2)
-            per_head = int(below + diag)
-        else:
-            per_head = int(bmk.sum()) * w.mb * w.mb
         if key_lens is not None:
             raise NotImplementedError("block mask combined with key padding")
+        bmk = np.asarray(block_mask).astype(bool)
+        mb = w.mb
+        if cs is None:
+            per_head = int(bmk.sum()) * mb * mb
+        else:
+            # pairs of block (I, J) under the causal rule depend on
+            # delta = I mb - J mb + cs only: sum over its rows r of
+            # clamp(delta + r + 1, 0, mb)
+            I, J = np.nonzero(bmk)
+            delta = (I - J) * mb + cs
+            r = np.arange(mb)
+            per_head = 0
+            for dl, cnt in zip(*np.unique(delta, return_counts=True)):
+                per_head += int(cnt) * int(np.clip(dl + r + 1, 0, mb).sum())
         return per_head * w.B * w.H
     total = 0
+    i = np.arange(Nq, dtype=np.int64)
     for b in range(w.B):
-        L = N if key_lens is None else max(0, min(N, int(key_lens[b])))
-        if w.causal:
-            # query i sees keys 0..min(i, L-1)
-            full = min(L, N)
-            pairs = full * (full + 1) // 2 + (N - full) * full
+        L = Nk if key_lens is None else max(0, min(Nk, int(key_lens[b])))
+        if cs is not None:
+            pairs = int(np.clip(i + cs + 1, 0, L).sum())
         else:
-            pairs = N * L
+            pairs = Nq * L
         total += pairs * w.H
     return total
+
+
+def forward_flops(w, pairs) -> float:
+    """Headline forward FLOP count: 4 B H N^2 d (halved when causal) for a
+    square problem, 4 d per visible pair otherwise."""
+    if w.N == w.Nk:
+        return 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    return 4.0 * w.d * pairs
 
 
 def traffic_from_profile(workload: str, kernel: str):
@@ -111,6 +127,9 @@ def cpu_baseline(w, inputs, budget_heads=1, dropout=None):
     except Exception:  # threadpoolctl missing: fall back to the environment
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     sl = (slice(0, 1), slice(0, budget_heads))
+    pairs_head = visible_pairs(w, None if inputs["key_lens"] is None else inputs["key_lens"].numpy(),
+                               None if inputs["block_mask"] is None else inputs["block_mask"].numpy()
+                               ) / (w.B * w.H)
     q, k, v, do = (as_f64(inputs[n][sl]) for n in ("q", "k", "v", "do"))
     lens = None if inputs["key_lens"] is None else inputs["key_lens"].numpy()[:1]
     bm = None if inputs["block_mask"] is None else inputs["block_mask"].numpy()
@@ -118,10 +137,10 @@ def cpu_baseline(w, inputs, budget_heads=1, dropout=None):
     oracle.backward(q, k, v, do, w.scale, causal=w.causal, key_lens=lens, block_mask=bm,
                     mb=w.mb or 128, dropout=dropout)
     dt = time.perf_counter() - t0
-    flops_fwd = 4.0 * budget_heads * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    flops_fwd = forward_flops(w, pairs_head * w.B * w.H) / (w.B * w.H) * budget_heads
     return {"value": round(3.5 * flops_fwd / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads, "kind": "oracle",
-            "sample": f"1 batch x {budget_heads} head(s) of {w.name} (N={w.N}, d={w.d}), "
+            "sample": f"1 batch x {budget_heads} head(s) of {w.name} (N_q={w.N}, N_k={w.Nk}, d={w.d}), "
                       f"fp64 numpy two-pass forward + analytic backward"
                       f"{'' if dropout is None else f' with dropout p={dropout[0]}'}, {dt:.1f} s; "
                       f"host os.cpu_count()={os.cpu_count()}"}
@@ -159,7 +178,8 @@ def main():
     if not w.backward:
         raise SystemExit(f"workload {w.name} is forward-only; bench times forward + backward")
     dev = torch.device("cuda:0")
-    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N_q={w.N} N_k={w.Nk} d={w.d} {w.dtype} "
+        f"causal={w.causal}")
     inputs = make_workload_inputs(w, seed=0)
     q, k, v, do = (inputs[n].to(dev) for n in ("q", "k", "v", "do"))
     kl = None if inputs["key_lens"] is None else inputs["key_lens"].to(dev)
@@ -177,8 +197,8 @@ def main():
                                        fa_bwd_workspace_bytes, fa_fwd_blocksparse)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(fa_bwd_workspace_bytes(q, scale=w.scale, causal=w.causal, key_lens=kl),
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    ws = torch.empty(fa_bwd_workspace_bytes(q, k, scale=w.scale, causal=w.causal, key_lens=kl),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     common = dict(scale=w.scale, causal=w.causal, key_lens=kl)
@@ -232,12 +252,11 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step; fwd {fwd_ms:.3f} ms, "
         f"bwd pre {pre_ms:.3f} / main {main_ms:.3f} / dq {dq_ms:.3f} ms")
 
-    f_fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
-    f_step = 3.5 * f_fwd
-    value = f_step / (ms_step * 1e-3) / 1e12
-
     pairs = visible_pairs(w, None if inputs["key_lens"] is None else inputs["key_lens"].numpy(),
                           None if inputs["block_mask"] is None else inputs["block_mask"].numpy())
+    f_fwd = forward_flops(w, pairs)
+    f_step = 3.5 * f_fwd
+    value = f_step / (ms_step * 1e-3) / 1e12
     kernels = {
         "fwd_kernel": (fwd_ms, 4.0 * w.d * pairs),
         "bwd_main_kernel": (main_ms, 8.0 * w.d * pairs),
@@ -263,7 +282,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_k": w.Nk, "d": w.d,
                    "causal": w.causal, "mask_block": w.mb, "key_padding": w.lens is not None,
                    "dropout": args.dropout},
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),

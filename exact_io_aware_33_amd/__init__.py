@@ -6,8 +6,9 @@ arguments: torch supplies device memory and the current HIP stream, every step
 of the computation runs in the library's HIP kernels.  There is no fallback:
 if the library is missing, the call raises.
 
-Tensors are ``[B, H, N, d]`` views with unit stride along d; Q, K, V, O, dO
-(and the gradients this module allocates) share one set of strides.
+Tensors are ``[B, H, N, d]`` views with unit stride along d: Q, O, dO and dQ
+([B, H, N_q, d]) share one set of strides, K, V, dK and dV ([B, H, N_k, d])
+another (N_q != N_k: cross-attention or decoding, causal aligned bottom-right).
 
 Dropout: every entry point takes ``dropout_p`` (0 = none), ``dropout_seed``
 (64-bit Philox key) and ``dropout_offset`` (32-bit counter word); the backward
@@ -52,13 +53,17 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _problem(q, scale, causal, key_lens, dropout_p=0.0, dropout_seed=0, dropout_offset=0):
-    if q.dim() != 4:
+def _problem(q, k, scale, causal, key_lens, dropout_p=0.0, dropout_seed=0, dropout_offset=0):
+    if q.dim() != 4 or k.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     B, H, N, d = q.shape
-    if q.stride(3) != 1:
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError("K/V must be [B, H, N_k, d] with the B, H, d of Q")
+    if k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("Q and K/V must share dtype and device")
+    if q.stride(3) != 1 or k.stride(3) != 1:
         raise ValueError("the head dimension must be contiguous (stride 1)")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -73,7 +78,8 @@ def _problem(q, scale, causal, key_lens, dropout_p=0.0, dropout_seed=0, dropout_
                   scale=float(scale), causal=1 if causal else 0, dtype=_DTYPES[q.dtype],
                   key_lens=None if key_lens is None else key_lens.data_ptr(),
                   dropout_p=float(dropout_p), dropout_offset=int(dropout_offset),
-                  dropout_seed=int(dropout_seed))
+                  dropout_seed=int(dropout_seed), seqlen_k=k.shape[2], reserved=0,
+                  k_stride_b=k.stride(0), k_stride_h=k.stride(1), k_stride_n=k.stride(2))
     return p, key_lens
 
 
@@ -81,7 +87,8 @@ def _same_layout(ref, *others):
     for t in others:
         if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype \
                 or t.device != ref.device:
-            raise ValueError("Q, K, V, O and dO must share shape, strides, dtype and device")
+            raise ValueError("Q, O, dO, dQ (and K, V, dK, dV) must share shape, strides, dtype "
+                             "and device")
 
 
 def _empty_like_layout(q):
@@ -91,8 +98,8 @@ def _empty_like_layout(q):
 def fa_fwd(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=None,
            dropout_p=0.0, dropout_seed=0, dropout_offset=0):
     """Exact attention forward; returns (O, LSE).  Calls fa_fwd."""
-    _same_layout(q, k, v)
-    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    _same_layout(k, v)
+    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
     o = _empty_like_layout(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     _same_layout(q, o)
@@ -106,31 +113,39 @@ def fa_fwd_blocksparse(q, k, v, block_mask, *, mask_block=128, scale=None, causa
                        dropout_offset=0):
     """Block-sparse forward; ``block_mask`` is uint8 [N/mb, N/mb] (shared by all heads)
     or [H, N/mb, N/mb].  Returns (O, LSE).  Calls fa_fwd_blocksparse."""
-    _same_layout(q, k, v)
-    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
-    bm, hstride = _mask(block_mask, q)
+    _same_layout(k, v)
+    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    bm, hstride = _mask(block_mask, q, k, mask_block)
     o = _empty_like_layout(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    _same_layout(q, o)
     lib = _lib.load()
     _lib.check(lib.fa_fwd_blocksparse(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
                                       _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(q)))
     return o, lse
 
 
-def _mask(block_mask, q):
+def _mask(block_mask, q, k, mask_block):
     if block_mask.dtype != torch.uint8 or block_mask.device != q.device:
         raise ValueError("block_mask must be a uint8 tensor on the device of q")
     bm = block_mask.contiguous()
-    if bm.dim() == 2:
+    mb = int(mask_block)
+    # the library checks mask_block against N_q and N_k (and rejects a block
+    # that does not divide them); the mask's extent, which it reads through a
+    # bare pointer, is checked here
+    nq, nk = q.shape[2], k.shape[2]
+    want = (nq // mb, nk // mb) if mb > 0 and nq % mb == 0 and nk % mb == 0 else None
+    if bm.dim() == 2 and (want is None or tuple(bm.shape) == want):
         return bm, 0
-    if bm.dim() == 3 and bm.shape[0] == q.shape[1]:
+    if bm.dim() == 3 and bm.shape[0] == q.shape[1] and (want is None or tuple(bm.shape[1:]) == want):
         return bm, bm.stride(0)
-    raise ValueError("block_mask must be [N/mb, N/mb] or [H, N/mb, N/mb]")
+    raise ValueError(f"block_mask must be [N_q/mb, N_k/mb] = {want} or [H, N_q/mb, N_k/mb]")
 
 
-def fa_bwd_workspace_bytes(q, *, scale=None, causal=False, key_lens=None) -> int:
-    """Workspace bytes fa_bwd needs for this problem.  Calls fa_bwd_workspace_bytes."""
-    p, _ = _problem(q, scale, causal, key_lens)
+def fa_bwd_workspace_bytes(q, k=None, *, scale=None, causal=False, key_lens=None) -> int:
+    """Workspace bytes fa_bwd needs for this problem (K defaults to the
+    shape of Q).  Calls fa_bwd_workspace_bytes."""
+    p, _ = _problem(q, q if k is None else k, scale, causal, key_lens)
     lib = _lib.load()
     n = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
     if n == 0:
@@ -138,17 +153,17 @@ def fa_bwd_workspace_bytes(q, *, scale=None, causal=False, key_lens=None) -> int
     return int(n)
 
 
-def _bwd_outputs(q, workspace, p, grads):
+def _bwd_outputs(q, k, workspace, p, grads):
     lib = _lib.load()
     need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     outs = []
-    for g in grads:
+    for like, g in zip((q, k, k), grads):
         if g is None:
-            g = _empty_like_layout(q)
+            g = _empty_like_layout(like)
         else:
-            _same_layout(q, g)
+            _same_layout(like, g)
         outs.append(g)
     return outs[0], outs[1], outs[2], workspace
 
@@ -156,9 +171,10 @@ def _bwd_outputs(q, workspace, p, grads):
 def fa_bwd(q, k, v, o, lse, do, *, scale=None, causal=False, key_lens=None, workspace=None,
            dq=None, dk=None, dv=None, dropout_p=0.0, dropout_seed=0, dropout_offset=0):
     """Gradients (dQ, dK, dV) of <dO, O>.  Calls fa_bwd."""
-    _same_layout(q, k, v, o, do)
-    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
-    dq, dk, dv, ws = _bwd_outputs(q, workspace, p, (dq, dk, dv))
+    _same_layout(q, o, do)
+    _same_layout(k, v)
+    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    dq, dk, dv, ws = _bwd_outputs(q, k, workspace, p, (dq, dk, dv))
     lib = _lib.load()
     _lib.check(lib.fa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
@@ -170,10 +186,11 @@ def fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, *, mask_block=128, scale
                        causal=False, key_lens=None, workspace=None, dq=None, dk=None, dv=None,
                        dropout_p=0.0, dropout_seed=0, dropout_offset=0):
     """Block-sparse gradients (dQ, dK, dV).  Calls fa_bwd_blocksparse."""
-    _same_layout(q, k, v, o, do)
-    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
-    bm, hstride = _mask(block_mask, q)
-    dq, dk, dv, ws = _bwd_outputs(q, workspace, p, (dq, dk, dv))
+    _same_layout(q, o, do)
+    _same_layout(k, v)
+    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    bm, hstride = _mask(block_mask, q, k, mask_block)
+    dq, dk, dv, ws = _bwd_outputs(q, k, workspace, p, (dq, dk, dv))
     lib = _lib.load()
     _lib.check(lib.fa_bwd_blocksparse(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
                                       _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
@@ -188,9 +205,10 @@ def fa_bwd_ex(q, k, v, o, lse, do, stages, *, block_mask=None, mask_block=128, s
     """One or more stages of the backward launch sequence (FA_BWD_PRE, _MAIN,
     _DQ bits), writing into caller-provided gradients and workspace.  Calls
     fa_bwd_ex; block_mask None selects the dense path."""
-    _same_layout(q, k, v, o, do, dq, dk, dv)
-    p, kl = _problem(q, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
-    bm, hstride = (None, 0) if block_mask is None else _mask(block_mask, q)
+    _same_layout(q, o, do, dq)
+    _same_layout(k, v, dk, dv)
+    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    bm, hstride = (None, 0) if block_mask is None else _mask(block_mask, q, k, mask_block)
     lib = _lib.load()
     _lib.check(lib.fa_bwd_ex(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
                              _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),

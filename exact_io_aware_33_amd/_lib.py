@@ -14,7 +14,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_bwd_blocksparse", "fa_bwd_ex", "fa_status_string", "fa_last_error",
            "fa_abi_version")
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class FaProblem(ctypes.Structure):
@@ -34,6 +34,11 @@ class FaProblem(ctypes.Structure):
         ("dropout_p", ctypes.c_float),
         ("dropout_offset", ctypes.c_uint32),
         ("dropout_seed", ctypes.c_uint64),
+        ("seqlen_k", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("k_stride_b", ctypes.c_int64),
+        ("k_stride_h", ctypes.c_int64),
+        ("k_stride_n", ctypes.c_int64),
     ]
 
 

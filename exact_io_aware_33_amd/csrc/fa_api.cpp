@@ -27,12 +27,20 @@ bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 
 int elem_size(int32_t dt) { return dt == FA_DTYPE_F32 ? 4 : 2; }
 
+int32_t keys_of(const fa_problem_t *p) { return p->seqlen_k ? p->seqlen_k : p->seqlen; }
+
+bool k_strides_default(const fa_problem_t *p) {
+  return p->k_stride_b == 0 && p->k_stride_h == 0 && p->k_stride_n == 0;
+}
+
 // Checks shared by every entry point.
 fa_status_t check_problem(const fa_problem_t *p) {
   if (!p) return fail(FA_ERR_INVALID, "problem pointer is NULL");
   if (p->batch <= 0 || p->heads <= 0 || p->seqlen <= 0)
     return fail(FA_ERR_INVALID, "batch, heads and seqlen must be >= 1 (got %d, %d, %d)", p->batch,
                 p->heads, p->seqlen);
+  if (p->seqlen_k < 0) return fail(FA_ERR_INVALID, "seqlen_k must be >= 0 (got %d)", p->seqlen_k);
+  if (p->reserved != 0) return fail(FA_ERR_INVALID, "reserved field must be 0");
   if (p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_F16 && p->dtype != FA_DTYPE_BF16)
     return fail(FA_ERR_INVALID, "unknown dtype %d", p->dtype);
   if (p->head_dim <= 0) return fail(FA_ERR_INVALID, "head_dim must be >= 1 (got %d)", p->head_dim);
@@ -40,16 +48,22 @@ fa_status_t check_problem(const fa_problem_t *p) {
     return fail(FA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", p->head_dim);
   if (!std::isfinite(p->scale) || p->scale < 0.f)
     return fail(FA_ERR_INVALID, "scale must be finite and >= 0");
-  const int64_t rows = (int64_t)p->batch * p->heads * p->seqlen;
-  if (rows * p->head_dim >= (int64_t(1) << 31) || rows >= (int64_t(1) << 31))
-    return fail(FA_ERR_UNSUPPORTED, "B*H*N*d exceeds the 32-bit index range");
+  const int64_t bh = (int64_t)p->batch * p->heads;
+  for (int64_t n : {(int64_t)p->seqlen, (int64_t)keys_of(p)})
+    if (bh * n * p->head_dim >= (int64_t(1) << 31))
+      return fail(FA_ERR_UNSUPPORTED, "B*H*N*d exceeds the 32-bit index range");
   const int es = elem_size(p->dtype);
-  if (p->stride_b < 0 || p->stride_h < 0 || p->stride_n < 0)
-    return fail(FA_ERR_INVALID, "strides must be non-negative");
-  if ((p->stride_b * es) % 16 || (p->stride_h * es) % 16 || (p->stride_n * es) % 16)
-    return fail(FA_ERR_INVALID, "strides must be multiples of 16 bytes");
-  if (p->stride_n < p->head_dim)
-    return fail(FA_ERR_INVALID, "stride_n (%lld) smaller than head_dim", (long long)p->stride_n);
+  const int64_t st[2][3] = {{p->stride_b, p->stride_h, p->stride_n},
+                            {p->k_stride_b, p->k_stride_h, p->k_stride_n}};
+  for (int t = 0; t < (k_strides_default(p) ? 1 : 2); ++t) {
+    if (st[t][0] < 0 || st[t][1] < 0 || st[t][2] < 0)
+      return fail(FA_ERR_INVALID, "strides must be non-negative");
+    if ((st[t][0] * es) % 16 || (st[t][1] * es) % 16 || (st[t][2] * es) % 16)
+      return fail(FA_ERR_INVALID, "strides must be multiples of 16 bytes");
+    if (st[t][2] < p->head_dim)
+      return fail(FA_ERR_INVALID, "%s (%lld) smaller than head_dim", t ? "k_stride_n" : "stride_n",
+                  (long long)st[t][2]);
+  }
   if (p->key_lens && !aligned16(p->key_lens))
     return fail(FA_ERR_INVALID, "key_lens must be 16-byte aligned");
   if (!std::isfinite(p->dropout_p) || p->dropout_p < 0.f || p->dropout_p >= 1.f)
@@ -73,9 +87,12 @@ fa_status_t check_tensor(const void *ptr, const char *name) {
 fa_status_t check_mask(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int64_t hstride) {
   if (!mask) return fail(FA_ERR_INVALID, "block_mask is NULL");
   if (mb <= 0) return fail(FA_ERR_INVALID, "mask_block must be >= 1 (got %d)", mb);
-  if (p->seqlen % mb) return fail(FA_ERR_INVALID, "mask_block %d does not divide N = %d", mb, p->seqlen);
+  if (p->seqlen % mb || keys_of(p) % mb)
+    return fail(FA_ERR_INVALID, "mask_block %d does not divide N_q = %d and N_k = %d", mb, p->seqlen,
+                keys_of(p));
   if (mb % 128) return fail(FA_ERR_UNSUPPORTED, "mask_block %d is not a multiple of 128", mb);
-  if (p->seqlen / mb > 1024) return fail(FA_ERR_UNSUPPORTED, "N / mask_block exceeds 1024");
+  if (p->seqlen / mb > 1024 || keys_of(p) / mb > 1024)
+    return fail(FA_ERR_UNSUPPORTED, "N / mask_block exceeds 1024");
   if (hstride < 0) return fail(FA_ERR_INVALID, "mask_head_stride must be >= 0");
   return FA_OK;
 }
@@ -84,11 +101,17 @@ fa::AttnParams make_params(const fa_problem_t *p) {
   fa::AttnParams a{};
   a.B = p->batch;
   a.H = p->heads;
-  a.N = p->seqlen;
+  a.Nq = p->seqlen;
+  a.Nk = keys_of(p);
   a.d = p->head_dim;
   a.sb = p->stride_b;
   a.sh = p->stride_h;
   a.sn = p->stride_n;
+  const bool same = k_strides_default(p);
+  a.ksb = same ? p->stride_b : p->k_stride_b;
+  a.ksh = same ? p->stride_h : p->k_stride_h;
+  a.ksn = same ? p->stride_n : p->k_stride_n;
+  a.cshift = a.Nk - a.Nq;
   a.scale = p->scale;
   a.scale_log2 = p->scale * fa::kLog2eHost;
   a.causal = p->causal != 0;
@@ -126,7 +149,8 @@ fa_status_t fwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
   if (sparse) {
     a.mask = mask;
     a.mb = mb;
-    a.nblk = p->seqlen / mb;
+    a.nblk_q = p->seqlen / mb;
+    a.nblk_k = keys_of(p) / mb;
     a.mask_hstride = hstride;
   }
   return hip_status(fa::launch_fwd(a, (fa_dtype_t)p->dtype, sparse, (hipStream_t)stream));
@@ -167,7 +191,8 @@ fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
   if (sparse) {
     a.mask = mask;
     a.mb = mb;
-    a.nblk = p->seqlen / mb;
+    a.nblk_q = p->seqlen / mb;
+    a.nblk_k = keys_of(p) / mb;
     a.mask_hstride = hstride;
   }
   return hip_status(fa::launch_bwd(a, (fa_dtype_t)p->dtype, sparse, stages, (hipStream_t)stream));

@@ -53,11 +53,11 @@ constexpr int kMaxMaskBlocksB = 1024;
 // 1. -D = -rowsum(dO * O) and LSE * log2(e).  One thread per row.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(AttnParams p) {
-  const int64_t rows = (int64_t)p.B * p.H * p.N;
+  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
   const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (row >= rows) return;
-  const int n = (int)(row % p.N);
-  const int64_t bh = row / p.N;
+  const int n = (int)(row % p.Nq);
+  const int64_t bh = row / p.Nq;
   const int b = (int)(bh / p.H), hh = (int)(bh % p.H);
   const int64_t off = (int64_t)b * p.sb + (int64_t)hh * p.sh + (int64_t)n * p.sn;
   const char *o = reinterpret_cast<const char *>(static_cast<const T *>(p.o_in) + off);
@@ -134,24 +134,26 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // the wave index is made explicitly uniform (it selects scalar operands)
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const int N = p.N;
-  const int nkt = (N + C::BKC - 1) / C::BKC;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int nkt = (Nk + C::BKC - 1) / C::BKC;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nkt;
   const int kt = logical - bh * nkt;
   const int b = bh / p.H, hh = bh - b * p.H;
-  const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;     // Q, dO
+  const int64_t kbase = (int64_t)b * p.ksb + (int64_t)hh * p.ksh;  // K, V, dK, dV
   const T *Q = static_cast<const T *>(p.q) + base;
-  const T *K = static_cast<const T *>(p.k) + base;
-  const T *V = static_cast<const T *>(p.v) + base;
+  const T *K = static_cast<const T *>(p.k) + kbase;
+  const T *V = static_cast<const T *>(p.v) + kbase;
   const T *dO = static_cast<const T *>(p.dout) + base;
-  T *dK = static_cast<T *>(p.dk) + base;
-  T *dV = static_cast<T *>(p.dv) + base;
-  const float *LSE = p.lse + (int64_t)bh * N;
-  const float *negD = p.ws_negd + (int64_t)bh * N;
+  T *dK = static_cast<T *>(p.dk) + kbase;
+  T *dV = static_cast<T *>(p.dv) + kbase;
+  const float *LSE = p.lse + (int64_t)bh * Nq;
+  const float *negD = p.ws_negd + (int64_t)bh * Nq;
 
-  int kv_len = N;
-  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
+  int kv_len = Nk;
+  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), Nk);
+  const int cs = CAUSAL ? p.cshift : 0;  // causal: key j visible to query i iff i >= j - cs
   const int k0 = kt * C::BKC;
   const int kw0 = k0 + 32 * wave;  // first key of this wave
   const int key = kw0 + l32;       // this lane's key (column of S)
@@ -159,9 +161,9 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // dV accumulates (P o Z / (1 - p))^T dO: the common factor goes here.
   const float vscale = DROP ? p.drop_scale : 1.f;
   auto store_dkdv = [&](const f32x16 *dkacc, const f32x16 *dvacc) {
-    if (key >= N) return;
-    T *krow = dK + (int64_t)key * p.sn;
-    T *vrow = dV + (int64_t)key * p.sn;
+    if (key >= Nk) return;
+    T *krow = dK + (int64_t)key * p.ksn;
+    T *vrow = dV + (int64_t)key * p.ksn;
 #pragma unroll
     for (int nb = 0; nb < C::NOB; ++nb)
 #pragma unroll
@@ -202,7 +204,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   }
 
   // ---- the list of query blocks this workgroup visits
-  const int nqb_all = (N + C::BQ - 1) / C::BQ;
+  const int nqb_all = (Nq + C::BQ - 1) / C::BQ;
   int nq, first_skip = 0, per = 1;
   if constexpr (SPARSE) {
     per = p.mb / C::BQ;
@@ -210,9 +212,12 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     const uint8_t *mcol = p.mask + (int64_t)hh * p.mask_hstride + kb;
     if (wave == 0) {
       int count = 0;
-      for (int i0 = 0; i0 < p.nblk; i0 += 64) {
+      for (int i0 = 0; i0 < p.nblk_q; i0 += 64) {
         const int i = i0 + lane;
-        const bool set = i < p.nblk && (!CAUSAL || i >= kb) && mcol[(int64_t)i * p.nblk] != 0;
+        // causal: query block i reaches this key tile iff its last query
+        // sees the tile's first key
+        const bool set = i < p.nblk_q && (!CAUSAL || (i + 1) * p.mb - 1 + cs >= k0) &&
+                         mcol[(int64_t)i * p.nblk_k] != 0;
         const uint64_t bal = __ballot(set);
         if (set) blist[count + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)i;
         count += __popcll(bal);
@@ -221,11 +226,12 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     }
     __syncthreads();
     const int nl = nlist_s;
-    if (CAUSAL && nl > 0 && blist[0] == kb) first_skip = (k0 - kb * p.mb) / C::BQ;
+    // causal: queries below k0 - cs see no key of this tile
+    if (CAUSAL && nl > 0) first_skip = min(per, max(0, k0 - cs - (int)blist[0] * p.mb) / C::BQ);
     nq = nl * per - first_skip;
   } else {
-    first_skip = CAUSAL ? k0 / C::BQ : 0;
-    nq = nqb_all - first_skip;
+    first_skip = CAUSAL ? max(0, k0 - cs) / C::BQ : 0;
+    nq = max(0, nqb_all - first_skip);
   }
   auto qblock_start = [&](int t) -> int {
     const int u = t + first_skip;
@@ -239,9 +245,9 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
 
   // ---- K, V rows of this wave as the B operands of S and dP
   frag kf[C::KSTEPS], vf[C::KSTEPS];
-  if (key < N) {
-    const T *kr = K + (int64_t)key * p.sn + h * (D / 2);
-    const T *vr = V + (int64_t)key * p.sn + h * (D / 2);
+  if (key < Nk) {
+    const T *kr = K + (int64_t)key * p.ksn + h * (D / 2);
+    const T *vr = V + (int64_t)key * p.ksn + h * (D / 2);
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
       kf[s] = *reinterpret_cast<const frag *>(kr + s * KPL);
@@ -261,11 +267,11 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // from the workspace by 4-byte LDS-DMA (waves 0 and 2 the one, 1 and 3 the
   // other, so every wave issues the same number of operations).  Rows past N
   // read zeros there too: with zero Q and dO rows they add nothing to dK, dV.
-  const uint32_t q_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
+  const uint32_t q_bytes = (uint32_t)(((int64_t)(Nq - 1) * p.sn + D) * E);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, q_bytes), dors = make_rsrc(dO, q_bytes);
   const i32x4 qwords = rsrc_words(Q, q_bytes), dowords = rsrc_words(dO, q_bytes);
-  const i32x4 statwords = (wave & 1) ? rsrc_words(negD, (uint32_t)N * 4u)
-                                     : rsrc_words(p.ws_lse2 + (int64_t)bh * N, (uint32_t)N * 4u);
+  const i32x4 statwords = (wave & 1) ? rsrc_words(negD, (uint32_t)Nq * 4u)
+                                     : rsrc_words(p.ws_lse2 + (int64_t)bh * Nq, (uint32_t)Nq * 4u);
   const uint32_t lds0 = lds_addr(smem);
   const int row_bytes = (int)(p.sn * E);
   int voff[C::CPTQ];
@@ -391,7 +397,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   auto softmax_grad = [&](const char *ql, int q0, f32x16 &S, f32x16 &DP, auto masked) {
     const float *ll = reinterpret_cast<const float *>(ql + C::LSE_OFF);
     const float *dd = reinterpret_cast<const float *>(ql + C::D_OFF);
-    const int lim_q = CAUSAL ? key - q0 : -1;  // query row qr visible iff qr >= lim_q
+    const int lim_q = CAUSAL ? key - cs - q0 : -1;  // query row qr visible iff qr >= lim_q
     uint32_t keepb[4];
     if constexpr (DROP) keep_bytes_key_col(keepb, p, bh, q0, key, lane);
 #pragma unroll
@@ -542,7 +548,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   if (DROP || k0 + C::BKC > kv_len) {
     n_masked = nq;
   } else if (CAUSAL) {
-    while (n_masked < nq && qblock_start(n_masked) < k0 + C::BKC) ++n_masked;
+    while (n_masked < nq && qblock_start(n_masked) < k0 + C::BKC - cs) ++n_masked;
   }
   // (SA, DA) holds the current block's products at the top of every trip.
   auto swap_ab = [&]() {
@@ -627,39 +633,41 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const int N = p.N;
-  const int nqt = (N + C::BR - 1) / C::BR;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int nqt = (Nq + C::BR - 1) / C::BR;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt;
   int qt = logical - bh * nqt;
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int b = bh / p.H, hh = bh - b * p.H;
-  const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;     // Q, dO, dQ
+  const int64_t kbase = (int64_t)b * p.ksb + (int64_t)hh * p.ksh;  // K, V
   const T *Q = static_cast<const T *>(p.q) + base;
-  const T *K = static_cast<const T *>(p.k) + base;
-  const T *V = static_cast<const T *>(p.v) + base;
+  const T *K = static_cast<const T *>(p.k) + kbase;
+  const T *V = static_cast<const T *>(p.v) + kbase;
   const T *dO = static_cast<const T *>(p.dout) + base;
   T *dQ = static_cast<T *>(p.dq) + base;
 
-  int kv_len = N;
-  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
+  int kv_len = Nk;
+  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), Nk);
+  const int cs = CAUSAL ? p.cshift : 0;  // causal: key j visible to query i iff j <= i + cs
   const int q_tile0 = qt * C::BR;
   const int qw0 = q_tile0 + 32 * wave;
   const int qi = qw0 + l32;
   int kv_hi = kv_len;
-  if (CAUSAL) kv_hi = min(kv_hi, q_tile0 + C::BR);
+  if (CAUSAL) kv_hi = min(kv_hi, q_tile0 + C::BR + cs);
 
   // ---- key tiles visited (as in the forward pass)
   int ntiles;
   int tiles_per_blk = 1;
   if constexpr (SPARSE) {
     tiles_per_blk = p.mb / C::BC;
-    const uint8_t *mrow = p.mask + (int64_t)hh * p.mask_hstride + (int64_t)(q_tile0 / p.mb) * p.nblk;
+    const uint8_t *mrow = p.mask + (int64_t)hh * p.mask_hstride + (int64_t)(q_tile0 / p.mb) * p.nblk_k;
     if (wave == 0) {
       int count = 0;
-      for (int j0 = 0; j0 < p.nblk; j0 += 64) {
+      for (int j0 = 0; j0 < p.nblk_k; j0 += 64) {
         const int j = j0 + lane;
-        const bool set = j < p.nblk && j * p.mb < kv_hi && mrow[j] != 0;
+        const bool set = j < p.nblk_k && j * p.mb < kv_hi && mrow[j] != 0;
         const uint64_t bal = __ballot(set);
         if (set) blist[count + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)j;
         count += __popcll(bal);
@@ -676,7 +684,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
       ntiles = (nl - 1) * tiles_per_blk + in_last;
     }
   } else {
-    ntiles = (kv_hi + C::BC - 1) / C::BC;
+    ntiles = kv_hi > 0 ? (kv_hi + C::BC - 1) / C::BC : 0;
   }
   auto tile_start = [&](int t) -> int {
     if constexpr (SPARSE) {
@@ -686,7 +694,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
       return t * C::BC;
     }
   };
-  const int lim = CAUSAL ? min(kv_len, q_tile0 + 1) : kv_len;
+  const int lim = CAUSAL ? min(kv_len, q_tile0 + 1 + cs) : kv_len;
   int n_full;
   if constexpr (SPARSE) {
     n_full = 0;
@@ -697,7 +705,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
     }
     n_full = min(n_full, ntiles);
   } else {
-    n_full = min(ntiles, lim / C::BC);
+    n_full = min(ntiles, max(lim, 0) / C::BC);
   }
 
   // ---- this wave's Q and dO rows (B operands), lse*log2(e) and D of the
@@ -705,7 +713,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   // addend), so the MFMA result is already dP - D.
   frag qf[C::KSTEPS], gf[C::KSTEPS];
   float lse2 = INFINITY, negdl = 0.f;
-  if (qi < N) {
+  if (qi < Nq) {
     const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
     const T *grow = dO + (int64_t)qi * p.sn + h * (D / 2);
 #pragma unroll
@@ -713,8 +721,8 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
       qf[s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
       gf[s] = *reinterpret_cast<const frag *>(grow + s * KPL);
     }
-    lse2 = p.ws_lse2[(int64_t)bh * N + qi];  // +inf when no key is visible: P = 0
-    negdl = p.ws_negd[(int64_t)bh * N + qi];
+    lse2 = p.ws_lse2[(int64_t)bh * Nq + qi];  // +inf when no key is visible: P = 0
+    negdl = p.ws_negd[(int64_t)bh * Nq + qi];
   } else {
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
@@ -729,11 +737,11 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   // ---- key tiles into the LDS ring (tile t -> slot t % NSLOT): buffer loads
   // with the tile start in the scalar offset, rows past N read as zeros
   // (16-bit: LDS-DMA, fp32: through registers).
-  const uint32_t kv_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)(Nk - 1) * p.ksn + D) * E);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, kv_bytes), vrs = make_rsrc(V, kv_bytes);
   const i32x4 kwords = rsrc_words(K, kv_bytes), vwords = rsrc_words(V, kv_bytes);
   const uint32_t lds0 = lds_addr(smem);
-  const int row_bytes = (int)(p.sn * E);
+  const int row_bytes = (int)(p.ksn * E);
   int voff[C::CPT];
 #pragma unroll
   for (int u = 0; u < C::CPT; ++u) {
@@ -843,7 +851,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   auto iter_any = [&](int j, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
     fetch(j + C::AHEAD);
     const char *kl = slot(j), *kn = slot(j + 1);
-    const int lim_o = (CAUSAL ? min(kv_len, qi + 1) : kv_len) - tile_start(j);
+    const int lim_o = (CAUSAL ? min(kv_len, qi + 1 + cs) : kv_len) - tile_start(j);
     uint32_t keepb[4];
     if constexpr (DROP) keep_bytes_query_col(keepb, p, bh, qi, tile_start(j), lane);
 #pragma unroll
@@ -943,7 +951,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   }
 
   // ---- dQ = scale * (dS K)
-  if (qi < N) {
+  if (qi < Nq) {
     T *qrow = dQ + (int64_t)qi * p.sn;
 #pragma unroll
     for (int nb = 0; nb < C::NOB; ++nb)
@@ -969,7 +977,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_main_t(const AttnParams &p, hipStream_t s) {
   using C = BwdCfg<T, D>;
-  const int64_t nkt = (p.N + C::BKC - 1) / C::BKC;
+  const int64_t nkt = (p.Nk + C::BKC - 1) / C::BKC;
   const int64_t grid = (int64_t)p.B * p.H * nkt;
   AttnParams a = p;
   void *args[] = {&a};
@@ -980,7 +988,7 @@ static hipError_t launch_main_t(const AttnParams &p, hipStream_t s) {
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_dq_t(const AttnParams &p, hipStream_t s) {
   using C = DqCfg<T, D>;
-  const int64_t nqt = (p.N + C::BR - 1) / C::BR;
+  const int64_t nqt = (p.Nq + C::BR - 1) / C::BR;
   const int64_t grid = (int64_t)p.B * p.H * nqt;
   AttnParams a = p;
   void *args[] = {&a};
@@ -992,7 +1000,7 @@ template <typename T, int D, bool DROP>
 static hipError_t launch_bwd_dd(const AttnParams &p, bool sparse, unsigned stages, hipStream_t s) {
   AttnParams a = p;
   void *args[] = {&a};
-  const int64_t rows = (int64_t)p.B * p.H * p.N;
+  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
   hipError_t e = hipSuccess;
   if (stages & FA_BWD_PRE) {
     e = hipLaunchKernel(reinterpret_cast<const void *>(&bwd_pre_kernel<T, D>),

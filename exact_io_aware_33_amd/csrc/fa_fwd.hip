@@ -119,38 +119,40 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const int N = p.N;
-  const int nqt = (N + C::BR - 1) / C::BR;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int nqt = (Nq + C::BR - 1) / C::BR;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt;
   int qt = logical - bh * nqt;
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int b = bh / p.H, hh = bh - b * p.H;
-  const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;
+  const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;     // Q, O
+  const int64_t kbase = (int64_t)b * p.ksb + (int64_t)hh * p.ksh;  // K, V
   const T *Q = static_cast<const T *>(p.q) + base;
-  const T *K = static_cast<const T *>(p.k) + base;
-  const T *V = static_cast<const T *>(p.v) + base;
+  const T *K = static_cast<const T *>(p.k) + kbase;
+  const T *V = static_cast<const T *>(p.v) + kbase;
   T *O = static_cast<T *>(p.o) + base;
 
-  int kv_len = N;
-  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), N);
+  int kv_len = Nk;
+  if (p.key_lens) kv_len = min(max(p.key_lens[b], 0), Nk);
+  const int cs = CAUSAL ? p.cshift : 0;  // causal: key j visible to query i iff j <= i + cs
   const int q_tile0 = qt * C::BR;
   const int qw0 = q_tile0 + C::QPW * wave;  // first query of this wave
   // this lane's query in query block qb is qw0 + 32*qb + l32
   int kv_hi = kv_len;                       // keys >= kv_hi are invisible to the whole tile
-  if (CAUSAL) kv_hi = min(kv_hi, q_tile0 + C::BR);
+  if (CAUSAL) kv_hi = min(kv_hi, q_tile0 + C::BR + cs);
 
   // ---- the list of key tiles this workgroup visits
   int ntiles;
   int tiles_per_blk = 1;
   if constexpr (SPARSE) {
     tiles_per_blk = p.mb / C::BC;
-    const uint8_t *mrow = p.mask + (int64_t)hh * p.mask_hstride + (int64_t)(q_tile0 / p.mb) * p.nblk;
+    const uint8_t *mrow = p.mask + (int64_t)hh * p.mask_hstride + (int64_t)(q_tile0 / p.mb) * p.nblk_k;
     if (wave == 0) {
       int count = 0;
-      for (int j0 = 0; j0 < p.nblk; j0 += 64) {
+      for (int j0 = 0; j0 < p.nblk_k; j0 += 64) {
         const int j = j0 + lane;
-        const bool set = j < p.nblk && j * p.mb < kv_hi && mrow[j] != 0;
+        const bool set = j < p.nblk_k && j * p.mb < kv_hi && mrow[j] != 0;
         const uint64_t bal = __ballot(set);
         if (set) blist[count + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)j;
         count += __popcll(bal);
@@ -167,7 +169,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
       ntiles = (nl - 1) * tiles_per_blk + in_last;
     }
   } else {
-    ntiles = (kv_hi + C::BC - 1) / C::BC;
+    ntiles = kv_hi > 0 ? (kv_hi + C::BC - 1) / C::BC : 0;
   }
   auto tile_start = [&](int t) -> int {
     if constexpr (SPARSE) {
@@ -185,7 +187,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = qw0 + 32 * qb + l32;
-    if (qi < N) {
+    if (qi < Nq) {
       const T *qrow = Q + (int64_t)qi * p.sn + h * (D / 2);
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) qf[qb][s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
@@ -199,11 +201,11 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
   // offset; rows past N read as zeros.  16-bit types: LDS-DMA, each wave
   // instruction writing 1 KB of the tile (lane i -> byte 16 i) and fetching
   // the chunk that the swizzle places there.  fp32: through registers.
-  const uint32_t kv_bytes = (uint32_t)(((int64_t)(N - 1) * p.sn + D) * E);
+  const uint32_t kv_bytes = (uint32_t)(((int64_t)(Nk - 1) * p.ksn + D) * E);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, kv_bytes), vrs = make_rsrc(V, kv_bytes);
   const i32x4 kwords = rsrc_words(K, kv_bytes), vwords = rsrc_words(V, kv_bytes);
   const uint32_t lds0 = lds_addr(smem);
-  const int row_bytes = (int)(p.sn * E);
+  const int row_bytes = (int)(p.ksn * E);
   int voff[C::CPT];
 #pragma unroll
   for (int u = 0; u < C::CPT; ++u) {
@@ -266,7 +268,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
   // Tiles that no mask touches form a prefix of the list (tiles ascend): a key
   // tile is whole for every query of the workgroup when it ends at or before
   // the padding length and (causal) at or before the tile's first query.
-  const int lim = CAUSAL ? min(kv_len, q_tile0 + 1) : kv_len;
+  const int lim = CAUSAL ? min(kv_len, q_tile0 + 1 + cs) : kv_len;
   int n_full;
   if constexpr (SPARSE) {
     n_full = 0;
@@ -277,7 +279,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
     }
     n_full = min(n_full, ntiles);
   } else {
-    n_full = min(ntiles, lim / C::BC);
+    n_full = min(ntiles, max(lim, 0) / C::BC);
   }
 
   // Operand fragments.  K fragment i (step s = i / NSB over d, key block
@@ -337,7 +339,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qi = qw0 + 32 * qb + l32;
-      const int lim_o = (CAUSAL ? min(kv_len, qi + 1) : kv_len) - kv0;
+      const int lim_o = (CAUSAL ? min(kv_len, qi + 1 + cs) : kv_len) - kv0;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -579,7 +581,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
     const float l_half = (lpart[qb][0] + lpart[qb][1]) + (lpart[qb][2] + lpart[qb][3]);
     const float l_tot = l_half + xor32(l_half);
     const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) / l_tot : 0.f;
-    if (qi < N) {
+    if (qi < Nq) {
       T *orow = O + (int64_t)qi * p.sn;
 #pragma unroll
       for (int nb = 0; nb < C::NOB; ++nb)
@@ -599,7 +601,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
           }
         }
       if (h == 0)
-        p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+        p.lse[(int64_t)bh * Nq + qi] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -607,7 +609,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_fwd_t(const AttnParams &p, hipStream_t s) {
   using C = FwdCfg<T, D, SPARSE>;
-  const int64_t nqt = (p.N + C::BR - 1) / C::BR;
+  const int64_t nqt = (p.Nq + C::BR - 1) / C::BR;
   const int64_t grid = (int64_t)p.B * p.H * nqt;
   AttnParams a = p;
   void *args[] = {&a};

@@ -23,16 +23,18 @@ struct AttnParams {
   float *ws_negd;     // [B*H*N]  -D = -rowsum(dO * O)
   float *ws_lse2;     // [B*H*N]  LSE * log2(e); +inf for rows that see no key
   // problem
-  int32_t B, H, N, d;
-  int64_t sb, sh, sn;        // element strides of the [B,H,N,d] tensors
+  int32_t B, H, Nq, Nk, d;   // N_q queries, N_k keys
+  int64_t sb, sh, sn;        // element strides of Q, O, dO, dQ ([B,H,N_q,d])
+  int64_t ksb, ksh, ksn;     // element strides of K, V, dK, dV ([B,H,N_k,d])
+  int32_t cshift;            // N_k - N_q: causal rule j <= i + cshift
   float scale;               // softmax scale
   float scale_log2;          // scale * log2(e)
   int32_t causal;
   const int32_t *key_lens;   // device [B] or nullptr
   // block sparsity
-  const uint8_t *mask;       // device [N/mb, N/mb] (+ head stride) or nullptr
+  const uint8_t *mask;       // device [N_q/mb, N_k/mb] (+ head stride) or nullptr
   int32_t mb;                // block size (multiple of 128)
-  int32_t nblk;              // N / mb
+  int32_t nblk_q, nblk_k;    // N_q / mb, N_k / mb
   int64_t mask_hstride;      // bytes between heads' masks (0 = shared)
   // dropout (Philox4x32-10 keep decisions); drop_thr == 0: none
   uint32_t drop_thr;         // t: an element whose decision byte is < t is dropped

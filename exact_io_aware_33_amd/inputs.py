@@ -6,12 +6,13 @@ it returns (the oracle the exact float64 upcast of the rounded values).
 
 Recipe (one numpy PCG64 generator per call, ``default_rng(seed)``), in this
 fixed draw order:
-  1. Q, K, V, then dO, each i.i.d. N(0, 1) of shape [B, H, N, d] in float64,
+  1. Q, K, V, then dO, each i.i.d. N(0, 1) in float64, Q and dO of shape
+     [B, H, N, d], K and V of shape [B, H, N_k, d] (N_k = N unless given),
      rounded to the storage dtype with round-to-nearest-even;
   2. key-padding lengths, if requested: integers uniform on [lo, hi], both
      ends inclusive, one per batch element (shared by all heads);
-  3. block mask, if requested: [N/mb, N/mb] uint8, off-diagonal blocks
-     Bernoulli(density), diagonal blocks forced to 1, shared by all heads.
+  3. block mask, if requested: [N/mb, N_k/mb] uint8, blocks Bernoulli(density),
+     then the diagonal (block i, i) forced to 1, shared by all heads.
 
 The workloads below stand in for the pages' benchmarks (GPT-2 at 1K, BERT-large
 at 512, long-context 16K, block-sparse): same shapes, synthetic values.
@@ -40,7 +41,12 @@ class Workload:
     mb: int | None = None            # block-mask granularity, or None
     density: float = 0.1
     backward: bool = True
+    n_keys: int | None = None        # N_k when it differs from N (queries)
     note: str = ""
+
+    @property
+    def Nk(self) -> int:
+        return self.N if self.n_keys is None else self.n_keys
 
     @property
     def scale(self) -> float:
@@ -62,6 +68,10 @@ WORKLOADS = {
                  note="long-context causal attention, d=128"),
         Workload("blocksparse_n16k", 1, 8, 16384, 64, "f16", mb=128, density=0.1,
                  note="block-sparse attention, 128x128 blocks, diagonal set"),
+        Workload("chunked_prefill_q4k_k16k", 1, 16, 4096, 64, "bf16", causal=True, n_keys=16384,
+                 note="4K new queries against a 16K-key context, causal aligned bottom-right"),
+        Workload("blocksparse_n64k", 1, 4, 65536, 64, "f16", mb=128, density=0.05,
+                 note="block-sparse attention at the 64K Path-256 length, 128x128 blocks"),
     ]
 }
 
@@ -71,18 +81,20 @@ def torch_dtype(name: str) -> torch.dtype:
 
 
 def make_inputs(B, H, N, d, dtype, *, seed=0, with_do=True, lens=None, mb=None,
-                density=0.1):
+                density=0.1, n_keys=None):
     """Draw one problem's inputs.  Returns a dict of CPU tensors:
 
-    q, k, v, (do): storage dtype, contiguous [B, H, N, d];
-    key_lens: int32 [B] or None;  block_mask: uint8 [N/mb, N/mb] or None.
+    q, (do): storage dtype, contiguous [B, H, N, d]; k, v: [B, H, N_k, d]
+    (N_k = n_keys, default N); key_lens: int32 [B] or None;
+    block_mask: uint8 [N/mb, N_k/mb] or None.
     """
     rng = np.random.default_rng(seed)
     td = _TORCH_DTYPE[dtype]
+    Nk = N if n_keys is None else n_keys
     out = {}
     names = ["q", "k", "v"] + (["do"] if with_do else [])
     for n in names:
-        x = rng.standard_normal((B, H, N, d))
+        x = rng.standard_normal((B, H, Nk if n in ("k", "v") else N, d))
         out[n] = torch.from_numpy(x).to(td).contiguous()
     out["key_lens"] = None
     if lens is not None:
@@ -90,9 +102,8 @@ def make_inputs(B, H, N, d, dtype, *, seed=0, with_do=True, lens=None, mb=None,
         out["key_lens"] = torch.from_numpy(rng.integers(lo, hi + 1, B).astype(np.int32))
     out["block_mask"] = None
     if mb is not None:
-        assert N % mb == 0
-        nb = N // mb
-        m = (rng.random((nb, nb)) < density).astype(np.uint8)
+        assert N % mb == 0 and Nk % mb == 0
+        m = (rng.random((N // mb, Nk // mb)) < density).astype(np.uint8)
         np.fill_diagonal(m, 1)
         out["block_mask"] = torch.from_numpy(m)
     return out
@@ -103,8 +114,9 @@ def make_workload_inputs(w: Workload, *, seed=0, B=None, H=None, N=None):
     B = w.B if B is None else B
     H = w.H if H is None else H
     N = w.N if N is None else N
+    Nk = w.Nk if N is None else N + (w.Nk - w.N)
     return make_inputs(B, H, N, w.d, w.dtype, seed=seed, with_do=w.backward,
-                       lens=w.lens, mb=w.mb, density=w.density)
+                       lens=w.lens, mb=w.mb, density=w.density, n_keys=Nk)
 
 
 def as_f64(t) -> np.ndarray | None:

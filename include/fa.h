@@ -5,7 +5,8 @@
  * What is computed (FlashAttention summary page, paper 2205.14135, section
  * "Problem and motivation"): for every batch b and head h,
  *     S = scale * Q K^T,   P = softmax(S) row by row,   O = P V,
- * with Q, K, V, O in R^{N x d}.  The score matrix S and the probabilities P
+ * with Q, O in R^{N_q x d} and K, V in R^{N_k x d} (N_q = N_k for
+ * self-attention; N_q != N_k for cross-attention and decoding).  The score matrix S and the probabilities P
  * never reach device memory: they live in registers one tile at a time
  * (same page, "Key ideas": tiling and recomputation; section "Incremental
  * softmax tracking": the running max / running sum update).
@@ -13,9 +14,12 @@
  * Masking (same page, "Key ideas", kernel-fusion bullet names masking; section
  * "Block-Sparse FlashAttention" defines the block mask).  Key j is visible to
  * query i iff every active rule allows it:
- *   causal      : j <= i                       (fa_problem_t.causal != 0)
+ *   causal      : j <= i + N_k - N_q           (fa_problem_t.causal != 0; the
+ *                                               queries are the last N_q
+ *                                               positions of the key sequence,
+ *                                               so j <= i when N_q = N_k)
  *   key padding : j < key_lens[b]              (fa_problem_t.key_lens != NULL;
- *                                               values are clamped to [0, N])
+ *                                               values are clamped to [0, N_k])
  *   block mask  : M[i / mb][j / mb] != 0        (the *_blocksparse entry points)
  * A query row with no visible key gets O = 0, LSE = -inf and zero gradients.
  *
@@ -46,18 +50,19 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Layout.  Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d] arrays of the problem's
- *   dtype, with element strides (stride_b, stride_h, stride_n) shared by all of
- *   them and a unit stride along d.  LSE is a contiguous float32 [B, H, N].
- *   A contiguous [B, H, N, d] array has strides (H*N*d, N*d, d); a [B, N, H, d]
- *   array has (N*H*d, d, H*d).
+ * Layout.  Q, O, dO, dQ are [B, H, N_q, d] arrays of the problem's dtype with
+ *   element strides (stride_b, stride_h, stride_n); K, V, dK, dV are
+ *   [B, H, N_k, d] arrays with strides (k_stride_b, k_stride_h, k_stride_n)
+ *   (all three 0: the Q strides); unit stride along d.  LSE is a contiguous
+ *   float32 [B, H, N_q].  A contiguous [B, H, N, d] array has strides
+ *   (H*N*d, N*d, d); a [B, N, H, d] array has (N*H*d, d, H*d).
  * Memory.  Every data pointer is a DEVICE pointer owned by the caller; the
  *   library never allocates, frees or keeps device memory between calls and
  *   holds no state, so concurrent calls on different streams are safe.
  * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *   enqueue work and return; the caller synchronises before reading results
  *   and keeps every buffer alive until then.
- * Alignment.  Q, K, V, O, dO, dQ, dK, dV must be 16-byte aligned and the three
+ * Alignment.  Q, K, V, O, dO, dQ, dK, dV must be 16-byte aligned and all six
  *   strides multiples of 16 bytes; LSE, key_lens and the workspace 16-byte
  *   aligned.
  * Errors.  Argument errors are detected on the host before any HIP call and
@@ -67,8 +72,9 @@
  *   across this boundary.  fa_last_error() gives a message for the last failed
  *   call on the calling thread.
  * Supported shapes.  dtype FP16 or BF16 with d in {64, 128}; dtype FP32 with
- *   d in {64, 128}.  N >= 1 (any value, not only multiples of the tile),
- *   B >= 1, H >= 1, B*H*N < 2^31.  scale finite and >= 0.
+ *   d in {64, 128}.  N_q, N_k >= 1 (any values, not only multiples of the
+ *   tile), B >= 1, H >= 1, B*H*N*d < 2^31 for N = N_q and N = N_k.  scale
+ *   finite and >= 0.
  */
 #ifndef EXACT_IO_AWARE_FA_H
 #define EXACT_IO_AWARE_FA_H
@@ -80,7 +86,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum fa_dtype {
   FA_DTYPE_F32 = 0,   /* IEEE float32 storage, float32 arithmetic            */
@@ -93,7 +99,8 @@ typedef enum fa_status {
   FA_ERR_INVALID = 1,      /* bad argument: NULL pointer, size <= 0, non-finite
                               or negative scale, dropout_p outside [0, 1),
                               workspace too small, block size that does not
-                              divide N, misaligned pointer                    */
+                              divide N_q and N_k, misaligned pointer, nonzero
+                              reserved field                                 */
   FA_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim / dtype pair,
                               block size not a multiple of 128, sizes over the
                               32-bit index range                              */
@@ -104,61 +111,71 @@ typedef enum fa_status {
 typedef struct fa_problem {
   int32_t batch;            /* B >= 1                                          */
   int32_t heads;            /* H >= 1                                          */
-  int32_t seqlen;           /* N >= 1: number of queries = number of keys      */
+  int32_t seqlen;           /* N_q >= 1: number of queries (and of keys unless
+                               seqlen_k is set)                               */
   int32_t head_dim;         /* d: 64 or 128                                    */
-  int64_t stride_b;         /* element stride between batches                  */
-  int64_t stride_h;         /* element stride between heads                    */
-  int64_t stride_n;         /* element stride between rows (tokens)            */
+  int64_t stride_b;         /* Q, O, dO, dQ: element stride between batches    */
+  int64_t stride_h;         /*   ... between heads                            */
+  int64_t stride_n;         /*   ... between rows (tokens)                    */
   float scale;              /* S = scale * Q K^T; finite, >= 0 (1/sqrt(d) usual) */
   int32_t causal;           /* nonzero: key j visible to query i only if j <= i */
   int32_t dtype;            /* fa_dtype_t                                      */
   const int32_t *key_lens;  /* device int32 [B] or NULL (no padding): keys
                                j >= key_lens[b] are masked for every query and
-                               head of batch b; clamped to [0, N] on device    */
+                               head of batch b; clamped to [0, N_k] on device  */
   float dropout_p;          /* probability of dropping an element of P, in
                                [0, 1); 0 = no dropout (then the two fields
                                below are ignored)                             */
   uint32_t dropout_offset;  /* fourth Philox counter word (e.g. a step count) */
   uint64_t dropout_seed;    /* Philox key                                     */
+  int32_t seqlen_k;         /* N_k: number of keys; 0 = N_q                    */
+  int32_t reserved;         /* must be 0                                      */
+  int64_t k_stride_b;       /* K, V, dK, dV: element stride between batches;
+                               all three k_stride_* 0 = the Q strides         */
+  int64_t k_stride_h;       /*   ... between heads                            */
+  int64_t k_stride_n;       /*   ... between rows (keys)                      */
 } fa_problem_t;
 
 /* Forward pass (summary page, "Incremental softmax tracking", steps 1-4).
- *   q, k, v : device [B,H,N,d] inputs (dtype), read only.
- *   o       : device [B,H,N,d] output (dtype), written in full (rows of fully
- *             masked queries are written as zeros).
- *   lse     : device float32 [B,H,N] output, contiguous, written in full.
+ *   q       : device [B,H,N_q,d] input (dtype), read only.
+ *   k, v    : device [B,H,N_k,d] inputs (dtype), read only.
+ *   o       : device [B,H,N_q,d] output (dtype), written in full (rows of
+ *             fully masked queries are written as zeros).
+ *   lse     : device float32 [B,H,N_q] output, contiguous, written in full.
  * Returns FA_OK once the work is enqueued on `stream`. */
 fa_status_t fa_fwd(const fa_problem_t *p, const void *q, const void *k,
                    const void *v, void *o, float *lse, void *stream);
 
 /* Block-sparse forward (summary page, section "Block-Sparse FlashAttention":
- * only the nonzero blocks of M in {0,1}^{N/mb x N/mb} are evaluated).
- *   block_mask       : device uint8 [N/mb, N/mb], row-major (row = query
+ * only the nonzero blocks of M in {0,1}^{N_q/mb x N_k/mb} are evaluated).
+ *   block_mask       : device uint8 [N_q/mb, N_k/mb], row-major (row = query
  *                      block, column = key block); nonzero = evaluate.
- *   mask_block       : mb, a positive multiple of 128 that divides N.
+ *   mask_block       : mb, a positive multiple of 128 that divides N_q and N_k.
  *   mask_head_stride : bytes between the masks of consecutive heads, or 0 for
  *                      one mask shared by all heads (the mask of head h is at
  *                      block_mask + h * mask_head_stride; one per head, shared
  *                      by all batches).
  * The other arguments and the causal / key_lens fields act as in fa_fwd; all
- * active masks are combined with AND.  N / mb must not exceed 1024. */
+ * active masks are combined with AND.  N_q / mb and N_k / mb must not exceed
+ * 1024. */
 fa_status_t fa_fwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
                                int32_t mask_block, int64_t mask_head_stride,
                                const void *q, const void *k, const void *v,
                                void *o, float *lse, void *stream);
 
 /* Size in bytes of the device workspace fa_bwd needs for problem p (0 if p is
- * invalid).  It holds two float32 per query row, rowsum(dO * O) and the saved
- * LSE rescaled to base 2: O(N) extra memory (summary page, "Complexity
- * analysis": O(N) beyond inputs and outputs). */
+ * invalid).  It holds two float32 per query row (B*H*N_q rows): rowsum(dO * O)
+ * and the saved LSE rescaled to base 2, O(N) extra memory (summary page,
+ * "Complexity analysis": O(N) beyond inputs and outputs). */
 size_t fa_bwd_workspace_bytes(const fa_problem_t *p);
 
 /* Backward pass: gradients of <dO, O> (summary page, "Key ideas",
  * recomputation bullet: S and P are rebuilt per tile from Q, K, V, O, LSE).
  *   q, k, v, o : the forward's inputs and output (dtype), read only.
- *   lse        : the forward's float32 [B,H,N] statistics, read only.
- *   dout       : device [B,H,N,d] upstream gradient dO (dtype), read only.
- *   dq, dk, dv : device [B,H,N,d] outputs (dtype), written in full.
+ *   lse        : the forward's float32 [B,H,N_q] statistics, read only.
+ *   dout       : device [B,H,N_q,d] upstream gradient dO (dtype), read only.
+ *   dq         : device [B,H,N_q,d] output (dtype), written in full.
+ *   dk, dv     : device [B,H,N_k,d] outputs (dtype), written in full.
  *   workspace  : device scratch of at least fa_bwd_workspace_bytes(p) bytes,
  *                owned by the caller, contents on entry ignored; it must not
  *                be shared with a concurrently running call.

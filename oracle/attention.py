@@ -61,16 +61,17 @@ def _block_mask_for_head(block_mask, h):
 
 
 def allowed_mask(rows, N, *, causal=False, key_len=None, block_mask=None, mb=128,
-                 n_queries=None):
-    """Boolean [len(rows), N]: True where query ``rows[r]`` may see key j < N.
+                 n_queries=None, cols=None):
+    """Boolean [len(rows), N] (or [len(rows), len(cols)]): True where query
+    ``rows[r]`` may see key j < N (j = cols[c] when ``cols`` is given).
 
     The allowed set is the AND of every active mask: causal
     (j <= i + N - n_queries; n_queries defaults to N, giving j <= i), key
     padding (j < key_len) and block (M[i//mb, j//mb] != 0).
     """
     rows = np.asarray(rows, dtype=np.int64)
-    cols = np.arange(N, dtype=np.int64)
-    a = np.ones((rows.size, N), dtype=bool)
+    cols = np.arange(N, dtype=np.int64) if cols is None else np.asarray(cols, dtype=np.int64)
+    a = np.ones((rows.size, cols.size), dtype=bool)
     if causal:
         shift = 0 if n_queries is None else N - int(n_queries)
         a &= cols[None, :] <= rows[:, None] + shift
@@ -234,19 +235,23 @@ def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=N
     dq_rows [R,d], dk_cols [C,d], dv_cols [C,d]).
 
     dQ_i needs only row i of P and dP.  dK_j and dV_j need column j of P and
-    dS for every query row i, hence every row's LSE and D_i = rowsum(P * dP):
-    a first pass over all rows (in chunks) computes them, a second forms the
-    selected columns.
+    dS for every query row i that sees key j, hence those rows' LSE and
+    D_i = rowsum(P * dP): a first pass over the selected rows and every row
+    that sees a selected column (in chunks) computes them, a second forms the
+    selected columns from those rows (the others have P_ij = 0 there).
     """
     q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
     Nq, N = q.shape[0], k.shape[0]
     mk = dict(causal=causal, key_len=key_len, block_mask=block_mask, mb=mb, n_queries=Nq)
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
-    lse_all = np.empty(Nq)
-    D_all = np.empty(Nq)
-    for r0 in range(0, Nq, chunk):
-        rr = np.arange(r0, min(Nq, r0 + chunk))
+    sees = allowed_mask(np.arange(Nq), N, cols=cols, **mk).any(axis=1)
+    sees[rows] = True
+    need = np.nonzero(sees)[0]
+    lse_all = np.full(Nq, np.nan)
+    D_all = np.full(Nq, np.nan)
+    for c0 in range(0, need.size, chunk):
+        rr = need[c0:c0 + chunk]
         s = float(scale) * (q[rr] @ k.T)
         a = allowed_mask(rr, N, **mk)
         s = np.where(a, s, -np.inf)
@@ -273,10 +278,10 @@ def gradients_sampled(q, k, v, do, scale, rows, cols, *, causal=False, key_len=N
     # selected columns: dK, dV
     dk_cols = np.zeros((cols.size, q.shape[1]))
     dv_cols = np.zeros((cols.size, v.shape[1]))
-    for r0 in range(0, Nq, chunk):
-        rr = np.arange(r0, min(Nq, r0 + chunk))
+    for c0 in range(0, need.size, chunk):
+        rr = need[c0:c0 + chunk]
         s = float(scale) * (q[rr] @ k[cols].T)
-        a = allowed_mask(rr, N, **mk)[:, cols]
+        a = allowed_mask(rr, N, cols=cols, **mk)
         s = np.where(a, s, -np.inf)
         lc = lse_all[rr]
         fin = np.isfinite(lc)

@@ -53,7 +53,7 @@ def test_exports_match_header(lib):
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fa_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.fa_abi_version() == _lib.ABI_VERSION == 3
 
 
 def test_status_strings(lib):
@@ -71,6 +71,8 @@ def test_status_strings(lib):
     ("seqlen", 1 << 30, UNSUPPORTED),
     ("dropout_p", -0.1, INVALID), ("dropout_p", 1.0, INVALID), ("dropout_p", 1.5, INVALID),
     ("dropout_p", float("nan"), INVALID), ("dropout_p", float("inf"), INVALID),
+    ("seqlen_k", -1, INVALID), ("seqlen_k", 1 << 30, UNSUPPORTED), ("reserved", 1, INVALID),
+    ("k_stride_n", 60, INVALID), ("k_stride_h", -64, INVALID), ("k_stride_b", 4, INVALID),
 ])
 def test_problem_rejected_before_any_hip_call(lib, field, value, status):
     p = prob(**{field: value})
@@ -166,3 +168,21 @@ def test_problem_struct_layout_matches_header(tmp_path):
     got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
     want = [getattr(_lib.FaProblem, f).offset for f in fields] + [ctypes.sizeof(_lib.FaProblem)]
     assert got == want
+
+
+@pytest.mark.parametrize("nq,nk,mb", [
+    (256, 320, 128),  # does not divide N_k
+    (384, 256, 256),  # does not divide N_q
+])
+def test_block_mask_must_divide_both_lengths(lib, nq, nk, mb):
+    p = prob(seqlen=nq, seqlen_k=nk, stride_b=3 * nq * 64, stride_h=nq * 64,
+             k_stride_b=3 * nk * 64, k_stride_h=nk * 64, k_stride_n=64)
+    assert lib.fa_fwd_blocksparse(ctypes.byref(p), A, mb, 0, A, A, A, A, A, None) == INVALID
+    assert "divide" in lib.fa_last_error().decode()
+
+
+def test_workspace_counts_query_rows_only(lib):
+    p = prob(seqlen=100, seqlen_k=5000, stride_b=3 * 100 * 64, stride_h=100 * 64,
+             k_stride_b=3 * 5000 * 64, k_stride_h=5000 * 64, k_stride_n=64)
+    need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+    assert 2 * 3 * 100 * 8 <= need <= 2 * 3 * 100 * 8 + 512

@@ -84,8 +84,9 @@ RECT_MUTANTS = [
      "                                 block_mask=bm, mb=mb, n_queries=N)",
      "a = allowed_mask(rows, Nk, causal=causal, key_len=lens[b],\n"
      "                                 block_mask=bm, mb=mb)"),
-    ("sampled D pass over key count", "    for r0 in range(0, Nq, chunk):\n        rr = np.arange(r0, min(Nq, r0 + chunk))\n        s = float(scale) * (q[rr] @ k.T)",
-     "    for r0 in range(0, N, chunk):\n        rr = np.arange(r0, min(N, r0 + chunk))\n        s = float(scale) * (q[rr] @ k.T)"),
+    ("sampled pass over the selected rows only", "    need = np.nonzero(sees)[0]\n", "    need = np.unique(rows)\n"),
+    ("sampled column mask over the wrong keys", "        a = allowed_mask(rr, N, cols=cols, **mk)",
+     "        a = allowed_mask(rr, N, **mk)[:, :cols.size]"),
 ]
 
 
