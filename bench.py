@@ -17,6 +17,11 @@ through fa_bwd_ex, all on torch's current stream.  Prints ONE JSON line on stdou
              current kernel sources, else null.
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
 
+A forward-only (decoding) workload is timed as one split-KV forward per step
+(fa_fwd_splitkv with the library's split count): value = algorithmic HBM
+bytes (Q, K, V read; O, LSE written) per second, roofline bound "hbm" on the
+split forward kernel.
+
 --dropout P runs the same step with fused dropout (probability P, Philox
 counter offset = step index, as a training loop would advance it); FLOPs are
 counted as without dropout (the keep decisions are not matrix work).
@@ -146,6 +151,64 @@ def cpu_baseline(w, inputs, budget_heads=1, dropout=None):
                       f"host os.cpu_count()={os.cpu_count()}"}
 
 
+def decode_main(args, w, dev):
+    """One split-KV forward per step on a forward-only (decoding) workload."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_33_amd import (fa_fwd_splitkv, fa_fwd_splitkv_num_splits,
+                                       fa_fwd_splitkv_workspace_bytes)
+    from exact_io_aware_33_amd.inputs import make_workload_inputs
+
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} N_q={w.N} N_k={w.Nk} d={w.d} {w.dtype} "
+        f"causal={w.causal} (forward only, split-KV)")
+    inputs = make_workload_inputs(w, seed=0)
+    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    splits = fa_fwd_splitkv_num_splits(q, k, scale=w.scale, causal=w.causal)
+    ws = torch.empty(fa_fwd_splitkv_workspace_bytes(q, k, splits, scale=w.scale, causal=w.causal),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa_fwd_splitkv(q, k, v, num_splits=splits, scale=w.scale, causal=w.causal, workspace=ws,
+                       out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        events[i][0].record(stream)
+        step()
+        events[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    e = q.element_size()
+    alg_bytes = (2 * w.B * w.H * w.Nk * w.d + 2 * w.B * w.H * w.N * w.d) * e + 4 * w.B * w.H * w.N
+    value = alg_bytes / (ms_step * 1e-3) / 1e9
+    achieved = alg_bytes / (ev_ms * 1e-3) / 1e9
+    log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (events {ev_ms:.4f} ms), "
+        f"{splits} splits")
+    out = {
+        "metric": "decode attention HBM GB/s (split-KV forward)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_k": w.Nk, "d": w.d,
+                   "causal": w.causal, "num_splits": splits},
+        "roofline": {"kernel": "fwd_kernel (split) + splitkv_merge_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": alg_bytes, "avg_launch_ms": round(ev_ms, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,9 +238,9 @@ def main():
         log("bench.py needs a GPU")
         sys.exit(1)
     w = WORKLOADS[args.workload]
-    if not w.backward:
-        raise SystemExit(f"workload {w.name} is forward-only; bench times forward + backward")
     dev = torch.device("cuda:0")
+    if not w.backward:
+        return decode_main(args, w, dev)
     log(f"[bench] workload {w.name}: B={w.B} H={w.H} N_q={w.N} N_k={w.Nk} d={w.d} {w.dtype} "
         f"causal={w.causal}")
     inputs = make_workload_inputs(w, seed=0)

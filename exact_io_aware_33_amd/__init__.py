@@ -25,7 +25,8 @@ import torch
 from . import _lib
 from ._lib import FaError, FaProblem
 
-__all__ = ["fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_ex",
+__all__ = ["fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
+           "fa_fwd_splitkv_workspace_bytes", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_ex",
            "fa_bwd_workspace_bytes", "FaError", "library_path", "load_library",
            "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_DQ", "FA_BWD_ALL"]
 
@@ -140,6 +141,48 @@ def _mask(block_mask, q, k, mask_block):
     if bm.dim() == 3 and bm.shape[0] == q.shape[1] and (want is None or tuple(bm.shape[1:]) == want):
         return bm, bm.stride(0)
     raise ValueError(f"block_mask must be [N_q/mb, N_k/mb] = {want} or [H, N_q/mb, N_k/mb]")
+
+
+def fa_fwd_splitkv_num_splits(q, k, *, scale=None, causal=False, key_lens=None) -> int:
+    """The split count the library picks for this problem.  Calls fa_fwd_splitkv_num_splits."""
+    p, _ = _problem(q, k, scale, causal, key_lens)
+    lib = _lib.load()
+    n = lib.fa_fwd_splitkv_num_splits(ctypes.byref(p))
+    if n <= 0:
+        raise FaError(_lib.FA_ERR_INVALID, lib.fa_last_error().decode())
+    return int(n)
+
+
+def fa_fwd_splitkv_workspace_bytes(q, k, num_splits=0, *, scale=None, causal=False,
+                                   key_lens=None) -> int:
+    """Workspace bytes fa_fwd_splitkv needs.  Calls fa_fwd_splitkv_workspace_bytes."""
+    p, _ = _problem(q, k, scale, causal, key_lens)
+    lib = _lib.load()
+    n = lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), int(num_splits))
+    if n == 0:
+        raise FaError(_lib.FA_ERR_INVALID, lib.fa_last_error().decode())
+    return int(n)
+
+
+def fa_fwd_splitkv(q, k, v, *, num_splits=0, block_mask=None, mask_block=128, scale=None,
+                   causal=False, key_lens=None, workspace=None, out=None, lse=None):
+    """Split-KV forward (decoding shapes); returns (O, LSE).  num_splits <= 0 lets the
+    library choose; block_mask None selects the dense path.  Calls fa_fwd_splitkv."""
+    _same_layout(k, v)
+    p, kl = _problem(q, k, scale, causal, key_lens)
+    bm, hstride = (None, 0) if block_mask is None else _mask(block_mask, q, k, mask_block)
+    o = _empty_like_layout(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    _same_layout(q, o)
+    lib = _lib.load()
+    if workspace is None:
+        need = lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), int(num_splits))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _lib.check(lib.fa_fwd_splitkv(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
+                                  int(num_splits), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(q)))
+    return o, lse
 
 
 def fa_bwd_workspace_bytes(q, k=None, *, scale=None, causal=False, key_lens=None) -> int:

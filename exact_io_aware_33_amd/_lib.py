@@ -10,7 +10,8 @@ FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
+EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
+           "fa_fwd_splitkv_workspace_bytes", "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_bwd_blocksparse", "fa_bwd_ex", "fa_status_string", "fa_last_error",
            "fa_abi_version")
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
@@ -67,6 +68,12 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = i32
     lib.fa_fwd_blocksparse.argtypes = [pp, vp, i32, i64, vp, vp, vp, vp, vp, vp]
     lib.fa_fwd_blocksparse.restype = i32
+    lib.fa_fwd_splitkv.argtypes = [pp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fa_fwd_splitkv.restype = i32
+    lib.fa_fwd_splitkv_num_splits.argtypes = [pp]
+    lib.fa_fwd_splitkv_num_splits.restype = i32
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [pp, i32]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [pp]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]

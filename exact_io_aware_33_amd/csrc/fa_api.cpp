@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <algorithm>
 
 #include "fa.h"
 #include "fa_internal.hpp"
@@ -156,6 +157,19 @@ fa_status_t fwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
   return hip_status(fa::launch_fwd(a, (fa_dtype_t)p->dtype, sparse, (hipStream_t)stream));
 }
 
+// Split count the library picks: about four workgroups per CU over 256 CUs,
+// at least four key tiles per range, at most 128 ranges.
+int32_t auto_splits(const fa_problem_t *p) {
+  const int64_t nqt = (p->seqlen + 127) / 128;
+  const int64_t base = (int64_t)p->batch * p->heads * nqt;
+  const int kt = fa::fwd_key_tile((fa_dtype_t)p->dtype);
+  const int64_t tiles = (keys_of(p) + kt - 1) / kt;
+  int64_t sp = (1024 + base - 1) / base;
+  sp = std::min<int64_t>(sp, std::max<int64_t>(1, tiles / 4));
+  sp = std::min<int64_t>(sp, 128);
+  return (int32_t)std::max<int64_t>(1, sp);
+}
+
 fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int64_t hstride,
                      bool sparse, const void *q, const void *k, const void *v, const void *o,
                      const float *lse, const void *dout, void *dq, void *dk, void *dv, void *ws,
@@ -241,6 +255,65 @@ fa_status_t fa_bwd_ex(const fa_problem_t *p, const uint8_t *block_mask, int32_t 
                       void *workspace, size_t workspace_bytes, uint32_t stages, void *stream) {
   return bwd_impl(p, block_mask, mask_block, mask_head_stride, block_mask != nullptr, q, k, v, o, lse,
                   dout, dq, dk, dv, workspace, workspace_bytes, stages, stream);
+}
+
+int32_t fa_fwd_splitkv_num_splits(const fa_problem_t *p) {
+  g_err[0] = 0;
+  if (check_problem(p) != FA_OK) return 0;
+  return auto_splits(p);
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(const fa_problem_t *p, int32_t num_splits) {
+  g_err[0] = 0;
+  if (check_problem(p) != FA_OK) return 0;
+  if (num_splits > 1024) {
+    fail(FA_ERR_INVALID, "num_splits must be <= 1024 (got %d)", num_splits);
+    return 0;
+  }
+  const int32_t sp = num_splits > 0 ? num_splits : auto_splits(p);
+  return fa::splitkv_total_bytes((int64_t)p->batch * p->heads * p->seqlen, p->head_dim, sp);
+}
+
+fa_status_t fa_fwd_splitkv(const fa_problem_t *p, const uint8_t *block_mask, int32_t mask_block,
+                           int64_t mask_head_stride, int32_t num_splits, const void *q, const void *k,
+                           const void *v, void *o, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  fa_status_t st;
+  if ((st = check_problem(p)) != FA_OK) return st;
+  if ((st = check_tensor(q, "q")) != FA_OK || (st = check_tensor(k, "k")) != FA_OK ||
+      (st = check_tensor(v, "v")) != FA_OK || (st = check_tensor(o, "o")) != FA_OK ||
+      (st = check_tensor(lse, "lse")) != FA_OK || (st = check_tensor(workspace, "workspace")) != FA_OK)
+    return st;
+  const bool sparse = block_mask != nullptr;
+  if (sparse && (st = check_mask(p, block_mask, mask_block, mask_head_stride)) != FA_OK) return st;
+  if (num_splits > 1024) return fail(FA_ERR_INVALID, "num_splits must be <= 1024 (got %d)", num_splits);
+  if (drop_threshold(p->dropout_p) != 0)
+    return fail(FA_ERR_UNSUPPORTED, "dropout is not built for the split-KV forward");
+  const int32_t sp = num_splits > 0 ? num_splits : auto_splits(p);
+  const int64_t rows = (int64_t)p->batch * p->heads * p->seqlen;
+  const size_t need = fa::splitkv_total_bytes(rows, p->head_dim, sp);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes,
+                need);
+  fa::AttnParams a = make_params(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.nsplit = sp;
+  a.part_o = static_cast<float *>(workspace);
+  a.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                         fa::splitkv_o_bytes(rows, p->head_dim, sp));
+  if (sparse) {
+    a.mask = block_mask;
+    a.mb = mask_block;
+    a.nblk_q = p->seqlen / mask_block;
+    a.nblk_k = keys_of(p) / mask_block;
+    a.mask_hstride = mask_head_stride;
+  }
+  return hip_status(fa::launch_fwd_splitkv(a, (fa_dtype_t)p->dtype, sparse, (hipStream_t)stream));
 }
 
 const char *fa_status_string(fa_status_t status) {

@@ -97,7 +97,10 @@ constexpr float kMaxSlack = 8.0f;
 
 // DROP: dropout on P (keep decisions regenerated per tile, see fa_dropout.hpp);
 // every tile then takes the generic iteration.
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+// SPLIT: the workgroup covers one of p.nsplit contiguous ranges of the key
+// tiles its query tile sees and writes an fp32 partial (O_s = sum p v / l_s,
+// LSE_s) for the merge kernel below.
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool SPLIT = false>
 // d = 64: registers bounded for three waves per SIMD (the few spills this
 // costs sit outside the tile loops); two with dropout, whose generator needs
 // the registers.
@@ -121,7 +124,9 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
   const int h = lane >> 5, l32 = lane & 31;
   const int Nq = p.Nq, Nk = p.Nk;
   const int nqt = (Nq + C::BR - 1) / C::BR;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int logical0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = SPLIT ? logical0 % p.nsplit : 0;
+  const int logical = SPLIT ? logical0 / p.nsplit : logical0;
   const int bh = logical / nqt;
   int qt = logical - bh * nqt;
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
@@ -171,7 +176,9 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
   } else {
     ntiles = kv_hi > 0 ? (kv_hi + C::BC - 1) / C::BC : 0;
   }
+  int tbase = 0;  // first tile of this workgroup's range (split-KV)
   auto tile_start = [&](int t) -> int {
+    t += tbase;
     if constexpr (SPARSE) {
       const int bi = t / tiles_per_blk;
       return (int)blist[bi] * p.mb + (t - bi * tiles_per_blk) * C::BC;
@@ -280,6 +287,15 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
     n_full = min(n_full, ntiles);
   } else {
     n_full = min(ntiles, max(lim, 0) / C::BC);
+  }
+  if constexpr (SPLIT) {
+    // this workgroup's range [t0, t1) of the tile list; the unmasked tiles
+    // stay a prefix of it
+    const int t0 = (int)((int64_t)ntiles * split / p.nsplit);
+    const int t1 = (int)((int64_t)ntiles * (split + 1) / p.nsplit);
+    n_full = min(max(n_full - t0, 0), t1 - t0);
+    tbase = t0;
+    ntiles = t1 - t0;
   }
 
   // Operand fragments.  K fragment i (step s = i / NSB over d, key block
@@ -581,6 +597,21 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
     const float l_half = (lpart[qb][0] + lpart[qb][1]) + (lpart[qb][2] + lpart[qb][3]);
     const float l_tot = l_half + xor32(l_half);
     const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) / l_tot : 0.f;
+    if constexpr (SPLIT) {
+      if (qi < Nq) {
+        const int64_t prow = ((int64_t)split * p.B * p.H + bh) * Nq + qi;
+        float *po = p.part_o + prow * D;
+#pragma unroll
+        for (int nb = 0; nb < C::NOB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4 *>(po + nb * 32 + 8 * i + 4 * h) =
+                f32x4{oacc[qb][nb][4 * i] * inv, oacc[qb][nb][4 * i + 1] * inv,
+                      oacc[qb][nb][4 * i + 2] * inv, oacc[qb][nb][4 * i + 3] * inv};
+        if (h == 0) p.part_lse[prow] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+      continue;
+    }
     if (qi < Nq) {
       T *orow = O + (int64_t)qi * p.sn;
 #pragma unroll
@@ -606,14 +637,56 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+// ---------------------------------------------------------------------------
+// Split-KV merge (summary page, section "Incremental softmax tracking": the
+// statistics of a row split into parts combine by rescaling each part's sum
+// with exp(part max - total max); here in log-sum-exp form, with each part's
+// output already divided by its own sum):
+//     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+// One wavefront per query row; lanes run along d.  Parts that saw no key
+// carry LSE_s = -inf and weigh 0; a row no part saw gets O = 0, LSE = -inf.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) splitkv_merge_kernel(AttnParams p) {
+  constexpr int PER = D / 64;  // elements per lane
+  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;  // whole wavefronts only
+  const int S = p.nsplit;
+  float m = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) m = fmaxf(m, p.part_lse[(int64_t)sp * rows + row]);
+  const int qi = (int)(row % p.Nq);
+  const int64_t bh = row / p.Nq;
+  const int b = (int)(bh / p.H), hh = (int)(bh % p.H);
+  T *orow = static_cast<T *>(p.o) + (int64_t)b * p.sb + (int64_t)hh * p.sh + (int64_t)qi * p.sn;
+  float acc[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) acc[c] = 0.f;
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int sp = 0; sp < S; ++sp) {
+      const int64_t prow = (int64_t)sp * rows + row;
+      const float w = expf(p.part_lse[prow] - m);  // exp(-inf) = 0 for empty parts
+      wsum += w;
+      const float *po = p.part_o + prow * D;
+#pragma unroll
+      for (int c = 0; c < PER; ++c) acc[c] = fmaf(w, po[lane + 64 * c], acc[c]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int c = 0; c < PER; ++c) orow[lane + 64 * c] = (T)(acc[c] * inv);
+  if (lane == 0) p.lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+}
+
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool SPLIT = false>
 static hipError_t launch_fwd_t(const AttnParams &p, hipStream_t s) {
   using C = FwdCfg<T, D, SPARSE>;
   const int64_t nqt = (p.Nq + C::BR - 1) / C::BR;
-  const int64_t grid = (int64_t)p.B * p.H * nqt;
+  const int64_t grid = (int64_t)p.B * p.H * nqt * (SPLIT ? p.nsplit : 1);
   AttnParams a = p;
   void *args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE, DROP>),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE, DROP, SPLIT>),
                          dim3((unsigned)grid), dim3(C::NTHR), args, 0, s);
 }
 
@@ -641,6 +714,41 @@ hipError_t launch_fwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream
     case FA_DTYPE_BF16: return launch_fwd_dt<__bf16>(p, sparse, s);
   }
   return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+static hipError_t launch_splitkv_d(const AttnParams &p, bool sparse, hipStream_t s) {
+  hipError_t e;
+  if (sparse)
+    e = p.causal ? launch_fwd_t<T, D, true, true, false, true>(p, s)
+                 : launch_fwd_t<T, D, false, true, false, true>(p, s);
+  else
+    e = p.causal ? launch_fwd_t<T, D, true, false, false, true>(p, s)
+                 : launch_fwd_t<T, D, false, false, false, true>(p, s);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
+  AttnParams a = p;
+  void *args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&splitkv_merge_kernel<T, D>),
+                         dim3((unsigned)((rows + 3) / 4)), dim3(256), args, 0, s);
+}
+
+template <typename T>
+static hipError_t launch_splitkv_dt(const AttnParams &p, bool sparse, hipStream_t s) {
+  return p.d == 64 ? launch_splitkv_d<T, 64>(p, sparse, s) : launch_splitkv_d<T, 128>(p, sparse, s);
+}
+
+hipError_t launch_fwd_splitkv(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s) {
+  switch (dt) {
+    case FA_DTYPE_F32: return launch_splitkv_dt<float>(p, sparse, s);
+    case FA_DTYPE_F16: return launch_splitkv_dt<_Float16>(p, sparse, s);
+    case FA_DTYPE_BF16: return launch_splitkv_dt<__bf16>(p, sparse, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+int fwd_key_tile(fa_dtype_t dt) {
+  return dt == FA_DTYPE_F32 ? FwdCfg<float, 64, false>::BC : FwdCfg<__bf16, 64, false>::BC;
 }
 
 }  // namespace fa

@@ -41,11 +41,21 @@ struct AttnParams {
   float drop_scale;          // 256 / (256 - t), the factor of kept elements
   uint32_t drop_key0, drop_key1;  // Philox key (seed low, high word)
   uint32_t drop_offset;      // fourth counter word
+  // split-KV forward: nsplit > 0 ranges of key tiles per query tile, each
+  // writing an fp32 partial (O_s normalised by its own sum, LSE_s)
+  int32_t nsplit;
+  float *part_o;             // [nsplit][B*H*N_q][d]
+  float *part_lse;           // [nsplit][B*H*N_q]
 };
 
 // Launchers (defined in fa_fwd.hip / fa_bwd.hip).  They assume validated
 // arguments and return hipSuccess or the launch error.
 hipError_t launch_fwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s);
+// Split-KV forward: p.nsplit ranges per query tile into p.part_o / p.part_lse,
+// then the merge into p.o / p.lse.
+hipError_t launch_fwd_splitkv(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s);
+// Key tiles per forward tile for a dtype (the unit a split range is made of).
+int fwd_key_tile(fa_dtype_t dt);
 // `stages`: bit set of FA_BWD_PRE / FA_BWD_MAIN / FA_BWD_DQ, run in that order.
 hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, unsigned stages,
                       hipStream_t s);
@@ -54,5 +64,14 @@ hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, unsigned 
 // -D = -rowsum(dO * O), then LSE in the base-2 domain.
 inline size_t ws_array_bytes(int64_t rows) { return (size_t)((rows * 4 + 255) / 256 * 256); }
 inline size_t ws_total_bytes(int64_t rows) { return 2 * ws_array_bytes(rows); }
+
+// Split-KV workspace: fp32 partial outputs [S][rows][d], then partial LSE
+// [S][rows], each 256-byte aligned.
+inline size_t splitkv_o_bytes(int64_t rows, int d, int splits) {
+  return (size_t)(((int64_t)splits * rows * d * 4 + 255) / 256 * 256);
+}
+inline size_t splitkv_total_bytes(int64_t rows, int d, int splits) {
+  return splitkv_o_bytes(rows, d, splits) + (size_t)(((int64_t)splits * rows * 4 + 255) / 256 * 256);
+}
 
 }  // namespace fa

@@ -72,6 +72,8 @@ WORKLOADS = {
                  note="4K new queries against a 16K-key context, causal aligned bottom-right"),
         Workload("blocksparse_n64k", 1, 4, 65536, 64, "f16", mb=128, density=0.05,
                  note="block-sparse attention at the 64K Path-256 length, 128x128 blocks"),
+        Workload("decode_q1_k32k", 8, 32, 1, 128, "bf16", causal=True, n_keys=32768, backward=False,
+                 note="decoding: one new query per sequence against a 32K-key cache (split-KV)"),
     ]
 }
 

@@ -163,6 +163,33 @@ fa_status_t fa_fwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
                                const void *q, const void *k, const void *v,
                                void *o, float *lse, void *stream);
 
+/* Split-KV forward, for decoding and other shapes with few query tiles per
+ * (batch, head) and many keys: the key tiles each 128-query tile sees are cut
+ * into num_splits contiguous ranges, one workgroup each, so that the launch
+ * fills the GPU; every range leaves a partial output (divided by its own
+ * exponential sum) and a partial LSE in fp32, and a merge kernel combines
+ * them with the summary page's merge equation (section "Incremental softmax
+ * tracking") in log-sum-exp form:
+ *     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * The result is the one fa_fwd / fa_fwd_blocksparse computes (up to rounding).
+ *   block_mask       : NULL for the dense path, else as for fa_fwd_blocksparse
+ *                      (mask_block, mask_head_stride as there).
+ *   num_splits       : 1..1024, or <= 0 for the library's choice
+ *                      (fa_fwd_splitkv_num_splits); more ranges than key tiles
+ *                      leave some ranges empty (they weigh 0 in the merge).
+ *   workspace        : device scratch of at least
+ *                      fa_fwd_splitkv_workspace_bytes(p, num_splits) bytes,
+ *                      caller-owned, contents on entry ignored, not shared with
+ *                      a concurrent call.
+ * Other arguments as for fa_fwd.  Dropout is not built for this path
+ * (dropout_p that rounds to t > 0 gives FA_ERR_UNSUPPORTED). */
+int32_t fa_fwd_splitkv_num_splits(const fa_problem_t *p);  /* >= 1; 0 if p is invalid */
+size_t fa_fwd_splitkv_workspace_bytes(const fa_problem_t *p, int32_t num_splits); /* 0 if invalid */
+fa_status_t fa_fwd_splitkv(const fa_problem_t *p, const uint8_t *block_mask, int32_t mask_block,
+                           int64_t mask_head_stride, int32_t num_splits, const void *q,
+                           const void *k, const void *v, void *o, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Size in bytes of the device workspace fa_bwd needs for problem p (0 if p is
  * invalid).  It holds two float32 per query row (B*H*N_q rows): rowsum(dO * O)
  * and the saved LSE rescaled to base 2, O(N) extra memory (summary page,

@@ -186,3 +186,47 @@ def test_workspace_counts_query_rows_only(lib):
              k_stride_b=3 * 5000 * 64, k_stride_h=5000 * 64, k_stride_n=64)
     need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
     assert 2 * 3 * 100 * 8 <= need <= 2 * 3 * 100 * 8 + 512
+
+
+def _splitkv(lib, p, splits=0, ws=A, ws_bytes=None, mask=None, mb=128):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), splits)
+    return lib.fa_fwd_splitkv(ctypes.byref(p), mask, mb, 0, splits, A, A, A, A, A, ws, ws_bytes, None)
+
+
+def test_splitkv_choice_and_workspace(lib):
+    p = prob(seqlen=1, seqlen_k=32768, stride_b=3 * 64, stride_h=64,
+             k_stride_b=3 * 32768 * 64, k_stride_h=32768 * 64, k_stride_n=64)
+    n = lib.fa_fwd_splitkv_num_splits(ctypes.byref(p))
+    assert 1 <= n <= 128
+    rows = 2 * 3 * 1
+    assert lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), 0) == \
+        lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), n)
+    need7 = lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), 7)
+    assert 7 * rows * (64 + 1) * 4 <= need7 <= 7 * rows * (64 + 1) * 4 + 512
+    assert lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), 1025) == 0
+    # a large problem gets a single split (the query tiles already fill the GPU)
+    big = prob(seqlen=16384, batch=4, heads=16, stride_b=16 * 16384 * 64, stride_h=16384 * 64)
+    assert lib.fa_fwd_splitkv_num_splits(ctypes.byref(big)) == 1
+
+
+@pytest.mark.parametrize("case,status", [
+    ("too_many_splits", INVALID), ("workspace_small", INVALID), ("workspace_null", INVALID),
+    ("dropout", UNSUPPORTED), ("mask_block", INVALID), ("bad_problem", INVALID),
+])
+def test_splitkv_rejected_before_any_hip_call(lib, case, status):
+    p = prob()
+    if case == "too_many_splits":
+        assert _splitkv(lib, p, splits=1025, ws_bytes=1 << 40) == status
+    elif case == "workspace_small":
+        need = lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), 4)
+        assert _splitkv(lib, p, splits=4, ws_bytes=need - 1) == status
+    elif case == "workspace_null":
+        assert _splitkv(lib, p, ws=0) == status
+    elif case == "dropout":
+        assert _splitkv(lib, prob(dropout_p=0.1), ws_bytes=1 << 40) == status
+    elif case == "mask_block":
+        assert _splitkv(lib, p, mask=A, mb=100, ws_bytes=1 << 40) == status
+    else:
+        assert _splitkv(lib, prob(seqlen=0), ws_bytes=1 << 40) == status
+    assert lib.fa_last_error()

@@ -1,0 +1,121 @@
+"""Parity of the split-KV forward (fa_fwd_splitkv) with the oracle.
+
+The split-KV path computes the same O and LSE as the plain forward; here it is
+checked against the fp64 oracle's forward on decoding shapes (few queries,
+many keys), with several split counts (one; more than the key tiles, so that
+some ranges are empty; the library's choice), every mask mode including empty
+rows, block masks, K/V in their own layout, and the decoding workload at full
+size (every row checked: it is forward only).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_33_amd import fa_fwd, fa_fwd_splitkv, fa_fwd_splitkv_num_splits
+from exact_io_aware_33_amd.inputs import WORKLOADS, as_f64, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-2}
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape
+    assert not np.isnan(x).any(), "NaN in GPU output (unwritten or invalid element)"
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(x), fin), "finite/infinite pattern differs"
+    assert np.array_equal(x[~fin], ref[~fin]), "non-finite values differ"
+    if not fin.any():
+        return 0.0
+    den = float(np.max(np.abs(ref[fin])))
+    num = float(np.max(np.abs(x[fin] - ref[fin])))
+    return num if den == 0.0 else num / den
+
+
+def check(B, H, Nq, Nk, d, dtype, splits, *, causal=False, lens=None, key_lens=None, mb=None,
+          density=0.4, seed=0, kv_bnhd=False):
+    say(f"case B={B} H={H} N_q={Nq} N_k={Nk} d={d} {dtype} splits={splits} causal={causal} "
+        f"lens={lens} key_lens={key_lens} mb={mb} kv_bnhd={kv_bnhd}")
+    inp = make_inputs(B, H, Nq, d, dtype, seed=seed, lens=lens, mb=mb, density=density, n_keys=Nk,
+                      with_do=False)
+    if key_lens is not None:
+        inp["key_lens"] = torch.tensor(key_lens, dtype=torch.int32)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    if kv_bnhd:
+        k, v = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (k, v))
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    kl = None if inp["key_lens"] is None else inp["key_lens"].cuda()
+    bm = None if mb is None else inp["block_mask"].cuda()
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), device="cuda", dtype=torch.float32)
+    fa_fwd_splitkv(q, k, v, num_splits=splits, block_mask=bm, mask_block=mb or 128, scale=scale,
+                   causal=causal, key_lens=kl, out=o, lse=lse)
+    torch.cuda.synchronize()
+    lens_np = None if inp["key_lens"] is None else np.clip(inp["key_lens"].numpy().astype(np.int64), 0, Nk)
+    ro, rlse = oracle.forward(*(as_f64(inp[n]) for n in ("q", "k", "v")), scale, causal=causal,
+                              key_lens=lens_np, block_mask=None if mb is None else inp["block_mask"].numpy(),
+                              mb=mb or 128)
+    errs = dict(o=rel_err(as_f64(o), ro), lse=rel_err(lse.cpu().numpy(), rlse))
+    say("  errors: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= TOL[dtype]}
+    assert not bad, f"over tolerance {TOL[dtype]}: {bad}"
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [1, 3, 0])
+@pytest.mark.parametrize("nq,nk", [(1, 4100), (4, 1000), (130, 2000)])
+def test_splitkv_decode_shapes(dtype, d, causal, splits, nq, nk):
+    check(2, 3, nq, nk, d, dtype, splits, causal=causal)
+
+
+def test_more_splits_than_key_tiles():
+    check(1, 2, 3, 100, 64, "bf16", 16, causal=True)       # 2 key tiles, 16 ranges
+
+
+def test_splitkv_padding_with_empty_rows():
+    check(3, 2, 5, 3000, 128, "f16", 7, key_lens=[0, 1777, 5000])
+
+
+def test_splitkv_blocksparse_and_kv_layout():
+    check(1, 2, 256, 1024, 64, "bf16", 5, causal=True, mb=128, seed=3)
+    check(2, 4, 2, 4100, 128, "bf16", 0, causal=True, kv_bnhd=True, seed=4)
+
+
+def test_library_choice_fills_the_gpu_for_decoding():
+    w = WORKLOADS["decode_q1_k32k"]
+    q = torch.empty(w.B, w.H, w.N, w.d, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty(w.B, w.H, w.Nk, w.d, dtype=torch.bfloat16, device="cuda")
+    n = fa_fwd_splitkv_num_splits(q, k, causal=True)
+    assert n * w.B * w.H >= 1024
+
+
+def test_workload_decode_q1_k32k_full():
+    """Every row of the decoding workload (forward only), against the oracle;
+    also agrees with the plain forward within the tolerance."""
+    w = WORKLOADS["decode_q1_k32k"]
+    o, lse = check(w.B, w.H, w.N, w.Nk, w.d, w.dtype, 0, causal=True, seed=0)
+    inp = make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed=0, n_keys=w.Nk, with_do=False)
+    o2, lse2 = fa_fwd(*(inp[n].cuda() for n in ("q", "k", "v")), scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert rel_err(as_f64(o), as_f64(o2)) <= TOL[w.dtype]
+    assert rel_err(lse.cpu().numpy(), lse2.cpu().numpy()) <= 1e-5
