@@ -151,6 +151,20 @@ def cpu_baseline(w, inputs, budget_heads=1, dropout=None):
                       f"host os.cpu_count()={os.cpu_count()}"}
 
 
+def calibration_copy(args, dev):
+    """One device-to-device copy of known size, for scaling the HBM counters."""
+    if not args.copy_calibration_mib:
+        return
+    import torch
+    n = args.copy_calibration_mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+    del src, dst
+
+
 def decode_main(args, w, dev):
     """One split-KV forward per step on a forward-only (decoding) workload."""
     import numpy as np
@@ -164,6 +178,7 @@ def decode_main(args, w, dev):
         f"causal={w.causal} (forward only, split-KV)")
     inputs = make_workload_inputs(w, seed=0)
     q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    calibration_copy(args, dev)
     splits = fa_fwd_splitkv_num_splits(q, k, scale=w.scale, causal=w.causal)
     ws = torch.empty(fa_fwd_splitkv_workspace_bytes(q, k, splits, scale=w.scale, causal=w.causal),
                      dtype=torch.uint8, device=dev)
@@ -203,7 +218,11 @@ def decode_main(args, w, dev):
                    "causal": w.causal, "num_splits": splits},
         "roofline": {"kernel": "fwd_kernel (split) + splitkv_merge_kernel", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (None if traffic_from_profile(w.name, "fwd_kernel") is None
+                                 or traffic_from_profile(w.name, "splitkv_merge_kernel") is None
+                                 else traffic_from_profile(w.name, "fwd_kernel")
+                                 + traffic_from_profile(w.name, "splitkv_merge_kernel")),
                      "bytes_per_launch": alg_bytes, "avg_launch_ms": round(ev_ms, 4)},
     }
     print(json.dumps(out), flush=True)
@@ -247,14 +266,7 @@ def main():
     q, k, v, do = (inputs[n].to(dev) for n in ("q", "k", "v", "do"))
     kl = None if inputs["key_lens"] is None else inputs["key_lens"].to(dev)
     bm = None if inputs["block_mask"] is None else inputs["block_mask"].to(dev)
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
-        del src, dst
+    calibration_copy(args, dev)
 
     from exact_io_aware_33_amd import (FA_BWD_DQ, FA_BWD_MAIN, FA_BWD_PRE, fa_bwd_ex,
                                        fa_bwd_workspace_bytes, fa_fwd_blocksparse)

@@ -157,14 +157,16 @@ fa_status_t fwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
   return hip_status(fa::launch_fwd(a, (fa_dtype_t)p->dtype, sparse, (hipStream_t)stream));
 }
 
-// Split count the library picks: about four workgroups per CU over 256 CUs,
-// at least four key tiles per range, at most 128 ranges.
+// Split count the library picks: about two workgroups per CU over 256 CUs
+// (a sweep over decoding shapes, 8K-128K keys, d = 64 and 128, put 512
+// workgroups within 2% of the best count everywhere), at least four key tiles
+// per range, at most 128 ranges.
 int32_t auto_splits(const fa_problem_t *p) {
   const int64_t nqt = (p->seqlen + 127) / 128;
   const int64_t base = (int64_t)p->batch * p->heads * nqt;
   const int kt = fa::fwd_key_tile((fa_dtype_t)p->dtype);
   const int64_t tiles = (keys_of(p) + kt - 1) / kt;
-  int64_t sp = (1024 + base - 1) / base;
+  int64_t sp = (512 + base - 1) / base;
   sp = std::min<int64_t>(sp, std::max<int64_t>(1, tiles / 4));
   sp = std::min<int64_t>(sp, 128);
   return (int32_t)std::max<int64_t>(1, sp);

@@ -106,7 +106,7 @@ def test_library_choice_fills_the_gpu_for_decoding():
     q = torch.empty(w.B, w.H, w.N, w.d, dtype=torch.bfloat16, device="cuda")
     k = torch.empty(w.B, w.H, w.Nk, w.d, dtype=torch.bfloat16, device="cuda")
     n = fa_fwd_splitkv_num_splits(q, k, causal=True)
-    assert n * w.B * w.H >= 1024
+    assert n * w.B * w.H >= 512
 
 
 def test_workload_decode_q1_k32k_full():
