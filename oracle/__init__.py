@@ -13,12 +13,16 @@ from them.
   method's own algorithm.
 * :mod:`oracle.dropout` -- the Philox4x32-10 generator and the dropout keep
   mask (used through the ``dropout=`` argument of the attention functions).
+* :mod:`oracle.reductions` -- row softmax and LayerNorm / GroupNorm, the other
+  streaming reductions, plus the moment merge used to pin them.
 """
 from .attention import (allowed_mask, forward, backward, forward_rows,
                         gradients_sampled, probabilities)
 from .streaming import merge_stats, streaming_forward
 from .dropout import keep_mask, keep_scale, drop_threshold, philox4x32_10
+from .reductions import softmax_rows, layernorm_rows, merge_moments, streaming_moments
 
 __all__ = ["allowed_mask", "forward", "backward", "forward_rows",
            "probabilities", "gradients_sampled", "merge_stats", "streaming_forward",
-           "keep_mask", "keep_scale", "drop_threshold", "philox4x32_10"]
+           "keep_mask", "keep_scale", "drop_threshold", "philox4x32_10",
+           "softmax_rows", "layernorm_rows", "merge_moments", "streaming_moments"]

@@ -22,10 +22,12 @@ import oracle.dropout
 from tests import test_oracle as pins
 from tests import test_oracle_dropout as drop_pins
 from tests import test_oracle_rect as rect_pins
+from tests import test_oracle_reductions as red_pins
 
 _ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(_ORACLE, "attention.py")
 DROP_SRC = os.path.join(_ORACLE, "dropout.py")
+RED_SRC = os.path.join(_ORACLE, "reductions.py")
 
 MUTANTS = [
     ("dQ without the scale", "dq[b, h, rows] = float(scale) * (ds @ kb)", "dq[b, h, rows] = (ds @ kb)"),
@@ -88,6 +90,29 @@ RECT_MUTANTS = [
     ("sampled column mask over the wrong keys", "        a = allowed_mask(rr, N, cols=cols, **mk)",
      "        a = allowed_mask(rr, N, **mk)[:, :cols.size]"),
 ]
+
+
+# Mistakes in the other streaming reductions, caught by their pins.
+RED_MUTANTS = [
+    ("sample variance (n - 1)", "var = ((x - mean[:, None]) ** 2).sum(axis=1) / L",
+     "var = ((x - mean[:, None]) ** 2).sum(axis=1) / (L - 1)"),
+    ("eps outside the square root", "rstd = 1.0 / np.sqrt(var + float(eps))",
+     "rstd = 1.0 / (np.sqrt(var) + float(eps))"),
+    ("affine index ignores the group", "return (r % groups) * cpg + e // inner", "return e // inner"),
+    ("affine index ignores the inner size", "return (r % groups) * cpg + e // inner",
+     "return (r % groups) * cpg + e % cpg"),
+    ("moment merge weights swapped", "mean = np.where(n > 0, ma + delta * nb / safe, 0.0)",
+     "mean = np.where(n > 0, ma + delta * na / safe, 0.0)"),
+    ("moment merge without the cross term", "m2 = m2a + m2b + delta * delta * na * nb / safe",
+     "m2 = m2a + m2b"),
+    ("softmax LSE without the max", "lse = np.where(valid, m + np.log(np.where(valid, l, 1.0)), -np.inf)",
+     "lse = np.where(valid, np.log(np.where(valid, l, 1.0)), -np.inf)"),
+    ("softmax not normalised", "y = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)",
+     "y = np.where(valid[:, None], e, 0.0)"),
+    ("empty softmax row not zero", "y = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)",
+     "y = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 1.0 / x.shape[1])"),
+]
+_RED = ("softmax_rows", "layernorm_rows", "merge_moments", "streaming_moments")
 
 
 # The pins: every test function of a pin module (tests/test_oracle.py, or
@@ -171,9 +196,17 @@ def test_rect_pins_kill_mutant(monkeypatch, label, old, new):
     assert _first_failing_pin(rect_pins) is not None, f"no rectangular pin catches the mutant: {label}"
 
 
+@pytest.mark.parametrize("label,old,new", RED_MUTANTS, ids=[m[0] for m in RED_MUTANTS])
+def test_reduction_pins_kill_mutant(monkeypatch, label, old, new):
+    mut = _load_mutant(old, new, RED_SRC)
+    for attr in _RED:
+        monkeypatch.setattr(oracle, attr, getattr(mut, attr))
+    assert _first_failing_pin(red_pins) is not None, f"no reduction pin catches the mutant: {label}"
+
+
 def test_pins_pass_on_the_real_oracle():
     """Sanity: the same harness finds no failing pin on the unmutated oracle."""
-    for p in (pins, drop_pins, rect_pins):
+    for p in (pins, drop_pins, rect_pins, red_pins):
         for name, fn, kwargs in _pin_calls(p):
             try:
                 fn(**kwargs)
