@@ -27,7 +27,8 @@ from ._lib import FaError, FaProblem
 
 __all__ = ["fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
            "fa_fwd_splitkv_workspace_bytes", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_ex",
-           "fa_bwd_workspace_bytes", "FaError", "library_path", "load_library",
+           "fa_bwd_workspace_bytes", "fa_softmax_rows", "fa_layernorm_rows", "fa_group_norm",
+           "FaError", "library_path", "load_library",
            "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_DQ", "FA_BWD_ALL"]
 
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ, FA_BWD_ALL = (_lib.FA_BWD_PRE, _lib.FA_BWD_MAIN,
@@ -257,3 +258,59 @@ def fa_bwd_ex(q, k, v, o, lse, do, stages, *, block_mask=None, mask_block=128, s
                              _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), int(stages), _stream(q)))
+
+
+def _rows_view(x):
+    """A 2-D [rows, cols] tensor with unit column stride: (rows, cols, ld)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with contiguous rows")
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    return x.shape[0], x.shape[1], x.stride(0)
+
+
+def fa_softmax_rows(x, *, out=None, lse=None):
+    """Row softmax of a 2-D tensor; returns (y, lse [rows] fp32).  Calls fa_softmax_rows."""
+    rows, cols, ld = _rows_view(x)
+    y = torch.empty_like(x) if out is None else out
+    _, _, ldy = _rows_view(y)
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    lse = torch.empty(rows, dtype=torch.float32, device=x.device) if lse is None else lse
+    lib = _lib.load()
+    _lib.check(lib.fa_softmax_rows(_DTYPES[x.dtype], rows, cols, _ptr(x), ld, _ptr(y), ldy, _ptr(lse),
+                                   _stream(x)))
+    return y, lse
+
+
+def fa_layernorm_rows(x, gamma=None, beta=None, *, eps=1e-5, groups=1, inner=1, out=None,
+                      mean=None, rstd=None):
+    """LayerNorm (groups = inner = 1) or GroupNorm rows of a 2-D tensor; returns
+    (y, mean, rstd).  Calls fa_layernorm_rows."""
+    rows, cols, ld = _rows_view(x)
+    y = torch.empty_like(x) if out is None else out
+    _, _, ldy = _rows_view(y)
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    nch = groups * (cols // inner)
+    for t in (gamma, beta):
+        if t is not None and (t.dtype != x.dtype or t.numel() != nch or not t.is_contiguous()):
+            raise ValueError(f"gamma / beta must be contiguous {x.dtype} of {nch} channels")
+    mean = torch.empty(rows, dtype=torch.float32, device=x.device) if mean is None else mean
+    rstd = torch.empty(rows, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    lib = _lib.load()
+    _lib.check(lib.fa_layernorm_rows(_DTYPES[x.dtype], rows, cols, _ptr(x), ld, _ptr(gamma), _ptr(beta),
+                                     float(eps), int(groups), int(inner), _ptr(y), ldy, _ptr(mean),
+                                     _ptr(rstd), _stream(x)))
+    return y, mean, rstd
+
+
+def fa_group_norm(x, groups, gamma=None, beta=None, *, eps=1e-5):
+    """GroupNorm of an [N, C, *] tensor through fa_layernorm_rows (rows = N * groups)."""
+    N, C = x.shape[0], x.shape[1]
+    S = x[0, 0].numel()
+    if C % groups:
+        raise ValueError("groups must divide C")
+    x2 = x.contiguous().view(N * groups, (C // groups) * S)
+    y, mean, rstd = fa_layernorm_rows(x2, gamma, beta, eps=eps, groups=groups, inner=S)
+    return y.view(x.shape), mean.view(N, groups), rstd.view(N, groups)

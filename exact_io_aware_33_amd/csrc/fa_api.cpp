@@ -318,6 +318,97 @@ fa_status_t fa_fwd_splitkv(const fa_problem_t *p, const uint8_t *block_mask, int
   return hip_status(fa::launch_fwd_splitkv(a, (fa_dtype_t)p->dtype, sparse, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+fa_status_t check_rows(int32_t dtype, int64_t rows, int64_t cols, const void *x, int64_t ld_x,
+                       void *y, int64_t ld_y) {
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (rows <= 0 || cols <= 0)
+    return fail(FA_ERR_INVALID, "rows and cols must be >= 1 (got %lld, %lld)", (long long)rows,
+                (long long)cols);
+  if (rows >= (int64_t(1) << 31) || cols >= (int64_t(1) << 31))
+    return fail(FA_ERR_UNSUPPORTED, "rows and cols must be < 2^31");
+  const uintptr_t es = (uintptr_t)elem_size(dtype);
+  if (ld_x < cols || ld_y < cols) return fail(FA_ERR_INVALID, "ld_x and ld_y must be >= cols");
+  if (!x || !y) return fail(FA_ERR_INVALID, "x and y must not be NULL");
+  if (reinterpret_cast<uintptr_t>(x) % es || reinterpret_cast<uintptr_t>(y) % es)
+    return fail(FA_ERR_INVALID, "x and y must be aligned to their element size");
+  return FA_OK;
+}
+
+// Whether every row of x and y starts 16-byte aligned (16-byte accesses).
+bool rows_vec(int32_t dtype, const void *x, int64_t ld_x, const void *y, int64_t ld_y) {
+  const int64_t es = elem_size(dtype);
+  return aligned16(x) && aligned16(y) && (ld_x * es) % 16 == 0 && (ld_y * es) % 16 == 0;
+}
+
+bool aligned4(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_softmax_rows(int32_t dtype, int64_t rows, int64_t cols, const void *x, int64_t ld_x,
+                            void *y, int64_t ld_y, float *lse, void *stream) {
+  g_err[0] = 0;
+  fa_status_t st;
+  if ((st = check_rows(dtype, rows, cols, x, ld_x, y, ld_y)) != FA_OK) return st;
+  if (lse && !aligned4(lse)) return fail(FA_ERR_INVALID, "lse is not 4-byte aligned");
+  fa::RedParams a{};
+  a.vec = rows_vec(dtype, x, ld_x, y, ld_y);
+  a.x = x;
+  a.y = y;
+  a.lse = lse;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ld_x;
+  a.ldy = ld_y;
+  a.groups = 1;
+  a.inner = 1;
+  a.cpg = cols;
+  return hip_status(fa::launch_softmax_rows(a, (fa_dtype_t)dtype, (hipStream_t)stream));
+}
+
+fa_status_t fa_layernorm_rows(int32_t dtype, int64_t rows, int64_t cols, const void *x, int64_t ld_x,
+                              const void *gamma, const void *beta, float eps, int32_t groups,
+                              int64_t inner, void *y, int64_t ld_y, float *mean, float *rstd,
+                              void *stream) {
+  g_err[0] = 0;
+  fa_status_t st;
+  if ((st = check_rows(dtype, rows, cols, x, ld_x, y, ld_y)) != FA_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.f) return fail(FA_ERR_INVALID, "eps must be finite and >= 0");
+  if (groups < 1 || inner < 1) return fail(FA_ERR_INVALID, "groups and inner must be >= 1");
+  if (cols % inner) return fail(FA_ERR_INVALID, "inner (%lld) must divide cols (%lld)", (long long)inner,
+                                (long long)cols);
+  const uintptr_t es = (uintptr_t)elem_size(dtype);
+  if ((gamma && (reinterpret_cast<uintptr_t>(gamma) % es)) ||
+      (beta && (reinterpret_cast<uintptr_t>(beta) % es)))
+    return fail(FA_ERR_INVALID, "gamma and beta must be aligned to their element size");
+  if ((mean && !aligned4(mean)) || (rstd && !aligned4(rstd)))
+    return fail(FA_ERR_INVALID, "mean and rstd must be 4-byte aligned");
+  fa::RedParams a{};
+  a.vec = rows_vec(dtype, x, ld_x, y, ld_y);
+  a.gvec = (!gamma || aligned16(gamma)) && (!beta || aligned16(beta));
+  a.x = x;
+  a.y = y;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.mean = mean;
+  a.rstd = rstd;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ld_x;
+  a.ldy = ld_y;
+  a.eps = eps;
+  a.groups = groups;
+  a.inner = inner;
+  a.cpg = cols / inner;
+  return hip_status(fa::launch_layernorm_rows(a, (fa_dtype_t)dtype, (hipStream_t)stream));
+}
+
 const char *fa_status_string(fa_status_t status) {
   switch (status) {
     case FA_OK: return "FA_OK";

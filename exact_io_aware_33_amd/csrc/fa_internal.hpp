@@ -48,6 +48,21 @@ struct AttnParams {
   float *part_lse;           // [nsplit][B*H*N_q]
 };
 
+// Row reductions (fa_reduce.hip): softmax, LayerNorm / GroupNorm.
+struct RedParams {
+  const void *x;
+  void *y;
+  const void *gamma, *beta;  // dtype [channels] or nullptr
+  float *lse, *mean, *rstd;  // fp32 [rows] outputs or nullptr
+  int64_t rows, cols, ldx, ldy;
+  float eps;
+  int64_t groups, inner, cpg;  // channel of element e of row r: (r % groups) * cpg + e / inner
+  bool vec;   // x and y rows start 16-byte aligned: 16-byte accesses
+  bool gvec;  // gamma and beta start 16-byte aligned
+};
+hipError_t launch_softmax_rows(const RedParams &p, fa_dtype_t dt, hipStream_t s);
+hipError_t launch_layernorm_rows(const RedParams &p, fa_dtype_t dt, hipStream_t s);
+
 // Launchers (defined in fa_fwd.hip / fa_bwd.hip).  They assume validated
 // arguments and return hipSuccess or the launch error.
 hipError_t launch_fwd(const AttnParams &p, fa_dtype_t dt, bool sparse, hipStream_t s);

@@ -251,6 +251,36 @@ fa_status_t fa_bwd_ex(const fa_problem_t *p, const uint8_t *block_mask,
                       void *dq, void *dk, void *dv, void *workspace,
                       size_t workspace_bytes, uint32_t stages, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Other streaming reductions (math-properties page, section 8: softmax-based
+ * routing and gating, LayerNorm and GroupNorm have attention's structure, a
+ * finite state updated block by block).  Row-wise over a [rows, cols] matrix
+ * of the given dtype whose rows start ld elements apart (ld >= cols; pointers
+ * aligned to the element size; rows that start 16-byte aligned are read and
+ * written 16 bytes at a time, others element by element); y may equal x.
+ * Device pointers, caller-owned; errors as for the attention entry points. */
+
+/* y = softmax(x) per row: y_j = exp(x_j - m) / l, m = max_j x_j,
+ * l = sum_j exp(x_j - m); lse (fp32 [rows], may be NULL) = m + ln l.  A row
+ * whose entries are all -inf gets y = 0 and lse = -inf.  The per-thread state
+ * (m, l) is merged across threads with the summary page's merge equation. */
+fa_status_t fa_softmax_rows(int32_t dtype, int64_t rows, int64_t cols, const void *x,
+                            int64_t ld_x, void *y, int64_t ld_y, float *lse, void *stream);
+
+/* LayerNorm / GroupNorm per row: mean = sum x / n, var = sum (x - mean)^2 / n,
+ * rstd = 1 / sqrt(var + eps), y_e = (x_e - mean) rstd gamma[c] + beta[c] with
+ * channel c = (row % groups) * (cols / inner) + e / inner.  LayerNorm:
+ * groups = 1, inner = 1 (c = e, gamma / beta of cols entries).  GroupNorm of
+ * an [N, C, S] input with G groups: rows = N G, cols = (C / G) S, groups = G,
+ * inner = S, gamma / beta of C entries.  gamma, beta: dtype, may be NULL
+ * (scale 1, shift 0); mean, rstd: fp32 [rows] outputs, may be NULL.  eps
+ * finite and >= 0; inner must divide cols.  The per-thread state
+ * (n, mean, M2) is merged with the Chan-Golub-LeVeque pairwise update. */
+fa_status_t fa_layernorm_rows(int32_t dtype, int64_t rows, int64_t cols, const void *x,
+                              int64_t ld_x, const void *gamma, const void *beta, float eps,
+                              int32_t groups, int64_t inner, void *y, int64_t ld_y, float *mean,
+                              float *rstd, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *fa_status_string(fa_status_t status);
 

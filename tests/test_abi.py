@@ -230,3 +230,31 @@ def test_splitkv_rejected_before_any_hip_call(lib, case, status):
     else:
         assert _splitkv(lib, prob(seqlen=0), ws_bytes=1 << 40) == status
     assert lib.fa_last_error()
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=7), INVALID), (dict(rows=0), INVALID), (dict(cols=0), INVALID),
+    (dict(ld_x=7, cols=8), INVALID), (dict(ld_y=12), INVALID), (dict(x=0), INVALID),
+    (dict(y=A + 1), INVALID), (dict(rows=1 << 31), UNSUPPORTED),
+])
+def test_softmax_rows_rejected(lib, args, status):
+    a = dict(dtype=_lib.FA_DTYPE_BF16, rows=4, cols=64, x=A, ld_x=64, y=A, ld_y=64, lse=A)
+    a.update(args)
+    assert lib.fa_softmax_rows(a["dtype"], a["rows"], a["cols"], a["x"], a["ld_x"], a["y"], a["ld_y"],
+                               a["lse"], None) == status
+    assert lib.fa_last_error()
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(groups=0), INVALID),
+    (dict(inner=0), INVALID), (dict(inner=5), INVALID), (dict(gamma=A + 1), INVALID),
+    (dict(mean=A + 2), INVALID), (dict(cols=0), INVALID),
+])
+def test_layernorm_rows_rejected(lib, args, status):
+    a = dict(dtype=_lib.FA_DTYPE_F16, rows=4, cols=64, x=A, ld_x=64, gamma=None, beta=None, eps=1e-5,
+             groups=1, inner=1, y=A, ld_y=64, mean=None, rstd=None)
+    a.update(args)
+    assert lib.fa_layernorm_rows(a["dtype"], a["rows"], a["cols"], a["x"], a["ld_x"], a["gamma"],
+                                 a["beta"], a["eps"], a["groups"], a["inner"], a["y"], a["ld_y"],
+                                 a["mean"], a["rstd"], None) == status
+    assert lib.fa_last_error()
