@@ -50,11 +50,12 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the HIP/C++ sources that make up libfa."""
+    """sha256 over the sources the attention kernels and their launches are
+    built from (all of csrc/ except the separate row-reduction kernels)."""
     csrc = os.path.join(ROOT, "exact_io_aware_33_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")) and name != "fa_reduce.hip":
             h.update(name.encode())
             h.update(open(os.path.join(csrc, name), "rb").read())
     h.update(open(os.path.join(ROOT, "include", "fa.h"), "rb").read())
@@ -228,38 +229,17 @@ def decode_main(args, w, dev):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dropout", type=float, default=0.0,
-                    help="fused dropout probability (0 = none)")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="first run one device copy of this many MiB (counter calibration)")
-    args = ap.parse_args()
+def time_attention(args, w, dev, steps, warmup):
+    """Time `steps` whole steps of workload `w` after `warmup` untimed ones.
 
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(every (batch, head) is independent, so more GPUs would split B*H with no "
-              "communication; that path is not built).", file=sys.stderr)
-        sys.exit(2)
-
+    Returns the inputs, the wall-clock ms per step and the HIP-event averages
+    (ms) of the forward and of the three backward launches."""
     import numpy as np
     import torch
 
     from exact_io_aware_33_amd import fa_fwd
-    from exact_io_aware_33_amd.inputs import WORKLOADS, make_workload_inputs
+    from exact_io_aware_33_amd.inputs import make_workload_inputs
 
-    if not torch.cuda.is_available():
-        log("bench.py needs a GPU")
-        sys.exit(1)
-    w = WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    if not w.backward:
-        return decode_main(args, w, dev)
     log(f"[bench] workload {w.name}: B={w.B} H={w.H} N_q={w.N} N_k={w.Nk} d={w.d} {w.dtype} "
         f"causal={w.causal}")
     inputs = make_workload_inputs(w, seed=0)
@@ -307,25 +287,163 @@ def main():
         if ev is not None:
             ev[4].record(stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} steps done")
+    log(f"[bench] warmup {warmup} steps done")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, events[i])
+    for i in range(steps):
+        step(warmup + i, events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step = (t1 - t0) * 1e3 / steps
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     pre_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     main_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
     dq_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
-    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step; fwd {fwd_ms:.3f} ms, "
+    log(f"[bench] timed {steps} steps: {ms_step:.3f} ms/step; fwd {fwd_ms:.3f} ms, "
         f"bwd pre {pre_ms:.3f} / main {main_ms:.3f} / dq {dq_ms:.3f} ms")
+
+    return inputs, ms_step, fwd_ms, pre_ms, main_ms, dq_ms
+
+
+def sweep_main(args, dev):
+    """The metric's sequence-length sweep: bf16, d=64, H=16, B=16384/N (the
+    same number of tokens at every N), N = 1K..16K, causal and not.  Forward
+    TFLOP/s from the forward's HIP events, fwd+bwd TFLOP/s from the wall clock
+    of whole steps, FLOPs by the headline count (4 B H N^2 d forward, halved
+    when causal; backward 2.5x)."""
+    from exact_io_aware_33_amd.inputs import Workload
+
+    rows = []
+    for causal in (False, True):
+        for N in (1024, 2048, 4096, 8192, 16384):
+            w = Workload(f"sweep_n{N}_{'causal' if causal else 'full'}", 16384 // N, 16, N, 64,
+                         "bf16", causal=causal)
+            _, ms_step, fwd_ms, pre_ms, main_ms, dq_ms = time_attention(
+                args, w, dev, args.steps, args.warmup)
+            f_fwd = forward_flops(w, None)
+            rows.append({"N": N, "B": w.B, "H": w.H, "causal": causal,
+                         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 1),
+                         "bwd_tflops": round(2.5 * f_fwd / ((pre_ms + main_ms + dq_ms) * 1e-3) / 1e12, 1),
+                         "fwd_bwd_tflops": round(3.5 * f_fwd / (ms_step * 1e-3) / 1e12, 1),
+                         "ms_per_step": round(ms_step, 4),
+                         "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
+                                       "bwd_main": round(main_ms, 4), "bwd_dq": round(dq_ms, 4)}})
+            log(f"[bench] sweep {rows[-1]}")
+    print(json.dumps({"metric": "attention TFLOP/s fwd & fwd+bwd, N=1K-16K d=64 bf16; % of MFMA peak",
+                      "unit": "TFLOP/s", "peak": MFMA_PEAK_TFLOPS["bf16"], "steps": args.steps,
+                      "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+                      "sweep": rows}), flush=True)
+
+
+def reductions_main(args, dev):
+    """The other streaming reductions: each case is timed with HIP events on
+    the launch stream over `steps` launches; achieved = algorithmic bytes (read
+    x and gamma / beta once, write y and the fp32 per-row statistics) over the
+    average launch duration, against the 8 TB/s HBM peak."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_33_amd import fa_layernorm_rows, fa_softmax_rows
+
+    g = torch.Generator(device="cpu").manual_seed(0)
+    cases = [
+        ("softmax_rows_16k_x_32k_bf16", "softmax", 16384, 32768, torch.bfloat16, 1, 1),
+        ("softmax_rows_256k_x_64_f32", "softmax", 262144, 64, torch.float32, 1, 1),
+        ("layernorm_64k_x_4096_bf16", "layernorm", 65536, 4096, torch.bfloat16, 1, 1),
+        ("groupnorm_n32_c512_s4096_g32_bf16", "layernorm", 32 * 32, 16 * 4096, torch.bfloat16,
+         32, 4096),
+    ]
+    rows_out = []
+    stream = torch.cuda.current_stream(dev)
+    for name, kind, R, L, dt, groups, inner in cases:
+        x = torch.randn(R, L, generator=g, dtype=torch.float32).to(dt).to(dev)
+        y = torch.empty_like(x)
+        stat1 = torch.empty(R, dtype=torch.float32, device=dev)
+        stat2 = torch.empty(R, dtype=torch.float32, device=dev)
+        e = x.element_size()
+        if kind == "softmax":
+            def run():
+                fa_softmax_rows(x, out=y, lse=stat1)
+            nbytes = 2 * R * L * e + 4 * R
+        else:
+            nch = groups * (L // inner)
+            gamma = torch.randn(nch, generator=g).to(dt).to(dev)
+            beta = torch.randn(nch, generator=g).to(dt).to(dev)
+
+            def run():
+                fa_layernorm_rows(x, gamma, beta, groups=groups, inner=inner, out=y,
+                                  mean=stat1, rstd=stat2)
+            nbytes = 2 * R * L * e + 2 * nch * e + 8 * R
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            run()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rows_out.append({"case": name, "rows": R, "cols": L, "dtype": str(dt).split(".")[-1],
+                         "groups": groups, "inner": inner, "avg_launch_ms": round(ms, 4),
+                         "alg_bytes": nbytes, "achieved_GBs": round(gbs, 1),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        log(f"[bench] {rows_out[-1]}")
+        del x, y
+    print(json.dumps({"metric": "streaming reductions, HBM GB/s of algorithmic bytes",
+                      "unit": "GB/s", "peak": HBM_PEAK_GBS, "bound": "hbm", "steps": args.steps,
+                      "warmup": args.warmup, "data": "synthetic", "cases": rows_out}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="fused dropout probability (0 = none)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line, print the metric's N=1K-16K sweep "
+                         "(bf16, d=64, H=16, B=16384/N, causal and not) as one JSON line")
+    ap.add_argument("--reductions", action="store_true",
+                    help="instead of the headline line, time the row softmax and LayerNorm / "
+                         "GroupNorm kernels (HBM-bound) and print one JSON line")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(every (batch, head) is independent, so more GPUs would split B*H with no "
+              "communication; that path is not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_io_aware_33_amd.inputs import WORKLOADS
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    if args.sweep:
+        return sweep_main(args, dev)
+    if args.reductions:
+        return reductions_main(args, dev)
+    if not w.backward:
+        return decode_main(args, w, dev)
+    inputs, ms_step, fwd_ms, pre_ms, main_ms, dq_ms = time_attention(
+        args, w, dev, args.steps, args.warmup)
 
     pairs = visible_pairs(w, None if inputs["key_lens"] is None else inputs["key_lens"].numpy(),
                           None if inputs["block_mask"] is None else inputs["block_mask"].numpy())
