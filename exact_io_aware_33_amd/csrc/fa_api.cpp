@@ -383,6 +383,8 @@ fa_status_t fa_layernorm_rows(int32_t dtype, int64_t rows, int64_t cols, const v
   if (groups < 1 || inner < 1) return fail(FA_ERR_INVALID, "groups and inner must be >= 1");
   if (cols % inner) return fail(FA_ERR_INVALID, "inner (%lld) must divide cols (%lld)", (long long)inner,
                                 (long long)cols);
+  if ((int64_t)groups * (cols / inner) >= (int64_t(1) << 31))
+    return fail(FA_ERR_UNSUPPORTED, "groups * cols / inner (the channel count) must be < 2^31");
   const uintptr_t es = (uintptr_t)elem_size(dtype);
   if ((gamma && (reinterpret_cast<uintptr_t>(gamma) % es)) ||
       (beta && (reinterpret_cast<uintptr_t>(beta) % es)))

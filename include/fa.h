@@ -274,7 +274,8 @@ fa_status_t fa_softmax_rows(int32_t dtype, int64_t rows, int64_t cols, const voi
  * an [N, C, S] input with G groups: rows = N G, cols = (C / G) S, groups = G,
  * inner = S, gamma / beta of C entries.  gamma, beta: dtype, may be NULL
  * (scale 1, shift 0); mean, rstd: fp32 [rows] outputs, may be NULL.  eps
- * finite and >= 0; inner must divide cols.  The per-thread state
+ * finite and >= 0; inner must divide cols; the channel count groups * cols /
+ * inner must be < 2^31 (FA_ERR_UNSUPPORTED otherwise).  The per-thread state
  * (n, mean, M2) is merged with the Chan-Golub-LeVeque pairwise update. */
 fa_status_t fa_layernorm_rows(int32_t dtype, int64_t rows, int64_t cols, const void *x,
                               int64_t ld_x, const void *gamma, const void *beta, float eps,

@@ -1,8 +1,9 @@
 """Parity of the row softmax and LayerNorm / GroupNorm kernels with the oracle.
 
-Every launch shape is covered: one wavefront per row (2100 rows) and one
-workgroup per row (few rows), each with the row held in registers and
-streamed twice; row lengths that leave a ragged last vector; strided rows;
+Every launch shape is covered: 8, 64, 256 or 1024 threads per row with the
+row held in registers (4, 8 or 16 vectors per thread), and rows streamed
+twice (unaligned or ragged rows, and rows too long to hold); row lengths
+that leave a ragged last vector; strided rows;
 -inf entries and an all -inf row (softmax); a large common offset (the
 moment merge must not lose the variance); GroupNorm through the same kernel;
 in-place calls.  Inputs are rounded to the storage type first; the oracle
@@ -53,8 +54,12 @@ def draw(rows, cols, dtype, seed, *, scale=1.0, offset=0.0, ld=None):
     return x, x.double().cpu().numpy()
 
 
+# Together these reach every launch shape the library picks (threads per row
+# 8 / 64 / 256 / 1024 with 4 / 8 / 16 vectors held per thread, and the rows
+# streamed twice) for both 16-bit types and fp32.
 SIZES = [(2100, 7), (2100, 1000), (2100, 4100), (2100, 9000), (3, 1), (3, 513), (3, 16384),
-         (3, 16390), (2, 70000)]
+         (3, 16390), (2, 70000), (5000, 64), (2500, 512), (1100, 4096), (1100, 8192),
+         (500, 8192), (3, 65536)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -114,7 +119,8 @@ def test_layernorm_large_offset_keeps_the_variance():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("N,C,S,G", [(2, 64, 49, 8), (3, 32, 1000, 4), (4, 16, 3, 16), (2, 12, 8, 3)])
+@pytest.mark.parametrize("N,C,S,G", [(2, 64, 49, 8), (3, 32, 1000, 4), (4, 16, 3, 16), (2, 12, 8, 3),
+                                     (2, 16, 4096, 4)])
 def test_group_norm(dtype, N, C, S, G):
     say(f"case groupnorm N={N} C={C} S={S} G={G} {dtype}")
     rng = np.random.default_rng(6)
