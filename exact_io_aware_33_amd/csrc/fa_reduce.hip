@@ -137,14 +137,20 @@ template <int TPR>
 struct RowGroup {
   static constexpr int NT = TPR > 256 ? TPR : 256;
   static constexpr int RPW = NT / TPR;
+
   int t;        // thread index within the row
   int64_t row;  // row of this thread's group
   __device__ __forceinline__ RowGroup()
-      : t((int)(threadIdx.x % TPR)), row((int64_t)blockIdx.x * RPW + threadIdx.x / TPR) {}
+      : t((int)(threadIdx.x % TPR)), row((int64_t)blockIdx.x * RPW + threadIdx.x / TPR) {
+    // One row per wave or per workgroup: say so, so that row addresses live
+    // in scalar registers and each held vector needs one 32-bit offset.
+    if constexpr (TPR >= 64) row = __builtin_amdgcn_readfirstlane((int)row);
+  }
 };
 
 template <typename T, int TPR, int NV>
-__global__ void __launch_bounds__(RowGroup<TPR>::NT) softmax_rows_kernel(RedParams p) {
+__global__ void __launch_bounds__(RowGroup<TPR>::NT)
+    softmax_rows_kernel(RedParams p) {
   using IO = RowVec<T>;
   constexpr int EPV = IO::EPV;
   __shared__ SmState lds[TPR > 64 ? TPR / 64 : 1];
@@ -181,7 +187,8 @@ __global__ void __launch_bounds__(RowGroup<TPR>::NT) softmax_rows_kernel(RedPara
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int64_t c = g.t + (int64_t)k * TPR;
-      keep[k] = *reinterpret_cast<const u32x4 *>(x + (c < nvec ? c : nvec - 1) * EPV);
+      keep[k] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x) +
+                                                 (uint32_t)((c < nvec ? c : nvec - 1) * 16));
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -246,7 +253,8 @@ __global__ void __launch_bounds__(RowGroup<TPR>::NT) softmax_rows_kernel(RedPara
 }
 
 template <typename T, int TPR, int NV>
-__global__ void __launch_bounds__(RowGroup<TPR>::NT) layernorm_rows_kernel(RedParams p) {
+__global__ void __launch_bounds__(RowGroup<TPR>::NT)
+    layernorm_rows_kernel(RedParams p) {
   using IO = RowVec<T>;
   constexpr int EPV = IO::EPV;
   __shared__ MoState lds[TPR > 64 ? TPR / 64 : 1];
@@ -271,7 +279,8 @@ __global__ void __launch_bounds__(RowGroup<TPR>::NT) layernorm_rows_kernel(RedPa
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int64_t c = g.t + (int64_t)k * TPR;
-      keep[k] = *reinterpret_cast<const u32x4 *>(x + (c < nvec ? c : nvec - 1) * EPV);
+      keep[k] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x) +
+                                                 (uint32_t)((c < nvec ? c : nvec - 1) * 16));
     }
     float sum = 0.f, n = 0.f;
 #pragma unroll
