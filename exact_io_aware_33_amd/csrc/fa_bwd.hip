@@ -50,11 +50,24 @@ constexpr int kMaxMaskBlocksB = 1024;
 
 
 // ---------------------------------------------------------------------------
-// 1. -D = -rowsum(dO * O) and LSE * log2(e).  One thread per row.
+// 1. -D = -rowsum(dO * O) and LSE * log2(e).  A row of O and of dO is
+// D * sizeof(T) / 16 (8, 16 or 32) sixteen-byte chunks; that many adjacent
+// lanes take one chunk each, so a wave reads whole consecutive rows (every
+// load instruction is one contiguous run of memory), and the partial dot
+// products meet by xor shuffles inside the lane group.
+template <typename T, int D>
+struct PreCfg {
+  static constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
+  static constexpr int RPB = 256 / LPR;                // rows per workgroup
+};
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(AttnParams p) {
+  using C = PreCfg<T, D>;
+  constexpr int EPC = 16 / (int)sizeof(T);
   const int64_t rows = (int64_t)p.B * p.H * p.Nq;
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * C::RPB + threadIdx.x / C::LPR;
+  const int c = (int)(threadIdx.x % C::LPR);
+  // LPR divides 64: a lane group lies in one wave and leaves together
   if (row >= rows) return;
   const int n = (int)(row % p.Nq);
   const int64_t bh = row / p.Nq;
@@ -62,17 +75,15 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(AttnParams p) {
   const int64_t off = (int64_t)b * p.sb + (int64_t)hh * p.sh + (int64_t)n * p.sn;
   const char *o = reinterpret_cast<const char *>(static_cast<const T *>(p.o_in) + off);
   const char *g = reinterpret_cast<const char *>(static_cast<const T *>(p.dout) + off);
-  constexpr int CH = D * (int)sizeof(T) / 16;
-  constexpr int EPC = 16 / (int)sizeof(T);
+  const u32x4 a = ldg16(o + 16 * c), bq = ldg16(g + 16 * c);
+  const T *ta = reinterpret_cast<const T *>(&a);
+  const T *tb = reinterpret_cast<const T *>(&bq);
   float acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const u32x4 a = ldg16(o + 16 * c), bq = ldg16(g + 16 * c);
-    const T *ta = reinterpret_cast<const T *>(&a);
-    const T *tb = reinterpret_cast<const T *>(&bq);
+  for (int e = 0; e < EPC; ++e) acc = fmaf((float)ta[e], (float)tb[e], acc);
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc = fmaf((float)ta[e], (float)tb[e], acc);
-  }
+  for (int w = C::LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
+  if (c != 0) return;
   // stored negated: the dP MFMAs accumulate onto it (acc = dP - D)
   p.ws_negd[row] = -acc;
   // the saved statistics in the base-2 domain: P = exp2(S*scale*log2e - lse2);
@@ -1003,8 +1014,9 @@ static hipError_t launch_bwd_dd(const AttnParams &p, bool sparse, unsigned stage
   const int64_t rows = (int64_t)p.B * p.H * p.Nq;
   hipError_t e = hipSuccess;
   if (stages & FA_BWD_PRE) {
+    constexpr int rpb = PreCfg<T, D>::RPB;
     e = hipLaunchKernel(reinterpret_cast<const void *>(&bwd_pre_kernel<T, D>),
-                        dim3((unsigned)((rows + 255) / 256)), dim3(256), args, 0, s);
+                        dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), args, 0, s);
     if (e != hipSuccess) return e;
   }
   if (stages & FA_BWD_MAIN) {
