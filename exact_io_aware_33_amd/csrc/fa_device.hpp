@@ -231,8 +231,8 @@ struct Layout {
 // Element e of MFMA step t in register order, from an LDS matrix with rows =
 // contraction index: M[row0 + reg_row(KPL*t + e, h)][col0 + l32].
 template <typename T, typename L>
-__device__ __forceinline__ typename Mma<T>::frag regorder_frag(const char *lds, int row0, int t, int col0) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ typename Mma<T>::frag regorder_frag(const char *lds, int row0, int t, int col0,
+                                                              int lane = threadIdx.x & 63) {
   if constexpr (Mma<T>::KPL == 1) {
     const int row = row0 + reg_row(t, lane >> 5);
     return *reinterpret_cast<const float *>(lds + L::off(row, (col0 + (lane & 31)) * 4));

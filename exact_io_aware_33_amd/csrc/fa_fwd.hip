@@ -120,8 +120,9 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
   __shared__ uint16_t blist[SPARSE ? kMaxMaskBlocks : 1];
   __shared__ int nlist_s;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  // Not const: recomputed after the steady loop (see there).
+  int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int Nq = p.Nq, Nk = p.Nk;
   const int nqt = (Nq + C::BR - 1) / C::BR;
   const int logical0 = xcd_remap(blockIdx.x, gridDim.x);
@@ -308,7 +309,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
   };
   auto vfrag = [&](const char *vl, int k, int nb) -> frag {
     const int sb = k / C::PSTEPS, t = k - sb * C::PSTEPS;
-    return regorder_frag<T, LT>(vl, sb * 32, t, nb * 32);
+    return regorder_frag<T, LT>(vl, sb * 32, t, nb * 32, lane);
   };
   constexpr int NS1 = NSB * C::PSTEPS;   // PV steps
   constexpr int NG1 = NS1 * C::NOB;      // PV groups (one V fragment, QB MFMAs each)
@@ -582,6 +583,17 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
       iter_steady(j++, odd{}, SB, SA);
       rotate();
     }
+  }
+  // The lane indices again, from an opaque copy of the thread id: what the
+  // tail iterations and the epilogue derive from them (LDS offsets, query
+  // rows) is then computed here instead of being hoisted above the steady
+  // loop and kept alive across it, where at this register budget it spilled.
+  {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    lane = t & 63;
+    h = lane >> 5;
+    l32 = lane & 31;
   }
   for (; j < ntiles; ++j) {
     iter_any(j, ffalse{}, SB, SA);
