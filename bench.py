@@ -307,6 +307,21 @@ def time_attention(args, w, dev, steps, warmup):
     log(f"[bench] timed {steps} steps: {ms_step:.3f} ms/step; fwd {fwd_ms:.3f} ms, "
         f"bwd pre {pre_ms:.3f} / main {main_ms:.3f} / dq {dq_ms:.3f} ms")
 
+    if getattr(args, "graph", False):
+        # The same step recorded once into a HIP graph and replayed: what the
+        # four launches cost without the host's per-launch overhead.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(0)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        time_attention.graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+        log(f"[bench] graph replay: {time_attention.graph_ms:.3f} ms/step")
     return inputs, ms_step, fwd_ms, pre_ms, main_ms, dq_ms
 
 
@@ -331,6 +346,9 @@ def sweep_main(args, dev):
                          "bwd_tflops": round(2.5 * f_fwd / ((pre_ms + main_ms + dq_ms) * 1e-3) / 1e12, 1),
                          "fwd_bwd_tflops": round(3.5 * f_fwd / (ms_step * 1e-3) / 1e12, 1),
                          "ms_per_step": round(ms_step, 4),
+                         **({"graph_fwd_bwd_tflops": round(
+                             3.5 * f_fwd / (time_attention.graph_ms * 1e-3) / 1e12, 1)}
+                            if args.graph else {}),
                          "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
                                        "bwd_main": round(main_ms, 4), "bwd_dq": round(dq_ms, 4)}})
             log(f"[bench] sweep {rows[-1]}")
@@ -429,6 +447,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line, print the metric's N=1K-16K sweep "
                          "(bf16, d=64, H=16, B=16384/N, causal and not) as one JSON line")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed "
+                         "(reported as graph_ms_per_step; value stays the eager step)")
     ap.add_argument("--reductions", action="store_true",
                     help="instead of the headline line, time the row softmax and LayerNorm / "
                          "GroupNorm kernels (HBM-bound) and print one JSON line")
@@ -494,6 +515,9 @@ def main():
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
         "bwd_tflops": round(2.5 * f_fwd / ((pre_ms + main_ms + dq_ms) * 1e-3) / 1e12, 3),
         "mfma_peak_frac_step": round(value / peak, 4),
+        **({"graph_ms_per_step": round(time_attention.graph_ms, 4),
+            "graph_tflops": round(f_step / (time_attention.graph_ms * 1e-3) / 1e12, 3)}
+           if args.graph else {}),
         "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
                       "bwd_main": round(main_ms, 4), "bwd_dq": round(dq_ms, 4)},
         "roofline": {"kernel": name, "bound": "mfma", "achieved": round(achieved, 3),
