@@ -481,6 +481,29 @@ def reductions_main(args, dev):
                       "warmup": args.warmup, "data": "synthetic", "cases": rows_out}), flush=True)
 
 
+def scaling_main(args, dev):
+    """One head count, growing N: B=1, H=16, d=64, bf16, non-causal, N = 2K,
+    4K, 8K, 16K, 32K.  Each N has its own grid size, so a rocprofv3 counter
+    run of this mode gives each kernel's HBM bytes as a function of N (the
+    pages' claim: Theta(N^2 d^2 / M) for the tiled method, against N^2 for
+    standard attention)."""
+    from exact_io_aware_33_amd.inputs import Workload
+
+    rows = []
+    for N in (2048, 4096, 8192, 16384, 32768):
+        w = Workload(f"scaling_n{N}", 1, 16, N, 64, "bf16")
+        _, ms_step, fwd_ms, pre_ms, main_ms, dq_ms = time_attention(args, w, dev, args.steps,
+                                                                    args.warmup)
+        f_fwd = forward_flops(w, None)
+        rows.append({"N": N, "fwd_bwd_tflops": round(3.5 * f_fwd / (ms_step * 1e-3) / 1e12, 1),
+                     "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
+                                   "bwd_main": round(main_ms, 4), "bwd_dq": round(dq_ms, 4)},
+                     "grid_workgroups": 16 * (N // 128)})
+        log(f"[bench] scaling {rows[-1]}")
+    print(json.dumps({"mode": "scaling", "B": 1, "H": 16, "d": 64, "dtype": "bf16", "causal": False,
+                      "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -498,6 +521,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed "
                          "(reported as graph_ms_per_step; value stays the eager step)")
+    ap.add_argument("--scaling", action="store_true",
+                    help="instead of the headline line, time fwd+bwd at B=1, H=16, d=64 bf16, "
+                         "non-causal, N = 2K..32K (for HBM-byte scaling under rocprofv3 counters)")
     ap.add_argument("--reductions", action="store_true",
                     help="instead of the headline line, time the row softmax and LayerNorm / "
                          "GroupNorm kernels (HBM-bound) and print one JSON line")
@@ -522,6 +548,8 @@ def main():
         return sweep_main(args, dev)
     if args.reductions:
         return reductions_main(args, dev)
+    if args.scaling:
+        return scaling_main(args, dev)
     if not w.backward:
         return decode_main(args, w, dev)
     inputs, ms_step, fwd_ms, pre_ms, main_ms, dq_ms = time_attention(
