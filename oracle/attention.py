@@ -16,8 +16,9 @@ What is computed, and where the pages define it
   P = exp(S - LSE) recovers the probabilities from it.
 * Masking is named in the same section's kernel-fusion bullet; the
   block-sparse section of that page defines the block mask M over row and
-  column blocks.  Readings (scale applied before masking, causal j <= i,
-  key padding j < len_b, block (i // mb, j // mb)) are listed in DESIGN.md.
+  column blocks.  The pages leave the details open; this oracle takes: the
+  scale applied before masking, causal j <= i, key padding j < len_b, and
+  element (i, j) governed by block (i // mb, j // mb).
   With N_q queries and N_k keys (N_q != N_k: cross-attention, decoding) the
   causal rule is aligned at the bottom right, j <= i + (N_k - N_q): the
   queries are the last N_q positions of the key sequence (the pages define
