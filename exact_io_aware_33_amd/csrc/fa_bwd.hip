@@ -147,9 +147,8 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   const int h = lane >> 5, l32 = lane & 31;
   const int Nq = p.Nq, Nk = p.Nk;
   const int nkt = (Nk + C::BKC - 1) / C::BKC;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nkt;
-  const int kt = logical - bh * nkt;
+  int bh, kt;  // causal: key tile 0 sees the most queries, so rank = kt is longest first
+  tile_of(blockIdx.x, gridDim.x, nkt, CAUSAL, bh, kt);
   const int b = bh / p.H, hh = bh - b * p.H;
   const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;     // Q, dO
   const int64_t kbase = (int64_t)b * p.ksb + (int64_t)hh * p.ksh;  // K, V, dK, dV
@@ -646,9 +645,8 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   const int h = lane >> 5, l32 = lane & 31;
   const int Nq = p.Nq, Nk = p.Nk;
   const int nqt = (Nq + C::BR - 1) / C::BR;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nqt;
-  int qt = logical - bh * nqt;
+  int bh, qt;
+  tile_of(blockIdx.x, gridDim.x, nqt, CAUSAL, bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int b = bh / p.H, hh = bh - b * p.H;
   const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;     // Q, dO, dQ

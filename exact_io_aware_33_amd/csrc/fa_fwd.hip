@@ -125,11 +125,16 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP
   int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int Nq = p.Nq, Nk = p.Nk;
   const int nqt = (Nq + C::BR - 1) / C::BR;
-  const int logical0 = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = SPLIT ? logical0 % p.nsplit : 0;
-  const int logical = SPLIT ? logical0 / p.nsplit : logical0;
-  const int bh = logical / nqt;
-  int qt = logical - bh * nqt;
+  int split = 0, bh, qt;
+  if constexpr (SPLIT) {
+    const int logical0 = xcd_remap(blockIdx.x, gridDim.x);
+    split = logical0 % p.nsplit;
+    const int logical = logical0 / p.nsplit;
+    bh = logical / nqt;
+    qt = logical - bh * nqt;
+  } else {
+    tile_of(blockIdx.x, gridDim.x, nqt, CAUSAL, bh, qt);
+  }
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int b = bh / p.H, hh = bh - b * p.H;
   const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;     // Q, O
