@@ -293,17 +293,19 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 // (batch*head, tile rank) of workgroup `id` in a launch of `total` = BH x
 // ntile workgroups.  Each XCD takes a contiguous range of heads, all of their
 // tiles (xcd_remap), in issue order.  Normally head by head; for causal
-// launches (rank 0 = the longest tile) of up to 128 tiles per head whose
+// launches (rank 0 = the longest tile) of up to 64 tiles per head whose
 // heads split evenly over the XCDs, rank-major instead: every head of the
 // XCD's range gets its rank-0 tile before any gets its rank-1 tile, so the
 // longest tiles of all heads start first and the short ones fill the end of
-// the launch.  The XCD's set of heads (what its L2 serves) is the same either
-// way.  Measured faster at every causal length from 1K to 16K (d = 64).
+// the launch.  The XCD's set of heads is the same either way, but rank-major
+// keeps all of them active at once: at 128 tiles per head (16K keys, d = 64)
+// their K and V no longer fit the XCD's 4 MB L2 together, HBM reads grew
+// 1.6-2x for a 1.4% faster step, so long sequences stay head by head.
 __device__ __forceinline__ void tile_of(int id, int total, int ntile, bool rank_major, int &bh,
                                         int &rank) {
   constexpr int kXcd = 8;
   const int nbh = total / ntile;
-  if (rank_major && ntile <= 128 && nbh % kXcd == 0) {
+  if (rank_major && ntile <= 64 && nbh % kXcd == 0) {
     const int hpx = nbh / kXcd;  // heads per XCD; total / 8 = hpx * ntile exactly
     const int xcd = id % kXcd, slot = id / kXcd;
     bh = xcd * hpx + slot % hpx;
