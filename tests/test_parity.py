@@ -144,6 +144,16 @@ def test_blocksparse_small(dtype, d, causal, mb):
     check_case(2, 2, 512, d, dtype, causal=causal, mb=mb, density=0.4, seed=mb + d)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,H,N,d,lens", [(2, 4, 1024, 64, None), (1, 8, 2048, 64, None),
+                                          (2, 8, 640, 128, (1, 640)), (1, 8, 4096, 64, None)])
+def test_causal_rank_major_tile_order(dtype, B, H, N, d, lens):
+    """Causal launches whose heads split evenly over the 8 XCDs and that have
+    at most 64 tiles per head are issued rank-major (longest tiles of every
+    head first): every (head, tile) must still be computed exactly once."""
+    check_case(B, H, N, d, dtype, causal=True, lens=lens, seed=3)
+
+
 def test_blocksparse_with_padding_and_empty_rows():
     nb = 4
     m = np.ones((nb, nb), np.uint8)
