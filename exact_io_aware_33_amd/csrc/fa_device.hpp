@@ -291,25 +291,37 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 }
 
 // (batch*head, tile rank) of workgroup `id` in a launch of `total` = BH x
-// ntile workgroups.  Each XCD takes a contiguous range of heads, all of their
-// tiles (xcd_remap), in issue order.  Normally head by head; for causal
-// launches (rank 0 = the longest tile) of up to 64 tiles per head whose
-// heads split evenly over the XCDs, rank-major instead: every head of the
-// XCD's range gets its rank-0 tile before any gets its rank-1 tile, so the
-// longest tiles of all heads start first and the short ones fill the end of
-// the launch.  The XCD's set of heads is the same either way, but rank-major
-// keeps all of them active at once: at 128 tiles per head (16K keys, d = 64)
-// their K and V no longer fit the XCD's 4 MB L2 together, HBM reads grew
-// 1.6-2x for a 1.4% faster step, so long sequences stay head by head.
+// ntile workgroups.  Workgroups go to the 8 XCDs round-robin by id; each XCD
+// takes whole heads (all their tiles), so a head's K/V re-reads stay in one
+// L2.  When the heads split evenly over the XCDs, XCD x takes heads x, x + 8,
+// x + 16, ...: every XCD then gets heads of every batch, and with key padding
+// (work per head proportional to its batch's key length) the XCDs stay
+// evenly loaded, which a contiguous range of heads (a few whole batches per
+// XCD) does not.  Otherwise each XCD takes a contiguous range (xcd_remap).
+// Within an XCD: head by head; or, for causal launches (rank 0 = the longest
+// tile) of up to 64 tiles per head, rank-major: every head of the XCD gets
+// its rank-0 tile before any gets its rank-1 tile, so the longest tiles of
+// all heads start first and the short ones fill the end of the launch.
+// Rank-major keeps all of the XCD's heads active at once: at 128 tiles per
+// head (16K keys, d = 64) their K and V no longer fit the XCD's 4 MB L2
+// together, HBM reads grew 1.6-2x for a 1.4% faster step, so long sequences
+// stay head by head.
 __device__ __forceinline__ void tile_of(int id, int total, int ntile, bool rank_major, int &bh,
                                         int &rank) {
   constexpr int kXcd = 8;
   const int nbh = total / ntile;
-  if (rank_major && ntile <= 64 && nbh % kXcd == 0) {
+  if (nbh % kXcd == 0) {
     const int hpx = nbh / kXcd;  // heads per XCD; total / 8 = hpx * ntile exactly
     const int xcd = id % kXcd, slot = id / kXcd;
-    bh = xcd * hpx + slot % hpx;
-    rank = slot / hpx;
+    int j;
+    if (rank_major && ntile <= 64) {
+      j = slot % hpx;
+      rank = slot / hpx;
+    } else {
+      j = slot / ntile;
+      rank = slot - j * ntile;
+    }
+    bh = xcd + kXcd * j;
   } else {
     const int logical = xcd_remap(id, total);
     bh = logical / ntile;
