@@ -19,9 +19,10 @@
 //
 // These kernels are bound by HBM bandwidth: the floor is one read of x and
 // one write of y.  A row of up to 16 vectors per thread (TPR x 16 x 16 bytes:
-// 2 KB at TPR = 8 up to 256 KB at TPR = 1024) stays in registers, packed as
-// loaded, between the two passes, so x is read from HBM exactly once and every
-// thread has all its loads in flight at once.  Longer rows are streamed twice
+// 2 KB at TPR = 8 up to 256 KB at TPR = 1024; LayerNorm up to 128 KB, 8 per
+// thread, at TPR = 1024) stays in registers, packed as loaded, between the
+// two passes, so x is read from HBM exactly once and every thread has all its
+// loads in flight at once.  Longer rows are streamed twice
 // (the second read mostly from L2 / MALL).  Short rows share a wavefront
 // (TPR = 8: eight rows per wave), so no lane idles on a 64-element row.
 #include <hip/hip_runtime.h>
