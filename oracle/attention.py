@@ -139,11 +139,14 @@ def _lens(key_lens, B):
 
 
 def forward(q, k, v, scale, *, causal=False, key_lens=None, block_mask=None,
-            mb=128, chunk=1024, dropout=None):
+            mb=128, chunk=1024, dropout=None, bh_offset=0):
     """Exact attention forward.  Returns (O [B,H,N,dv], LSE [B,H,N]) in fp64.
 
     N is the number of query rows; K and V may hold a different number of
-    rows (keys), and V a different width dv.
+    rows (keys), and V a different width dv.  ``bh_offset`` is added to the
+    (batch, head) index b*H + h that the dropout keep mask is drawn for, so
+    that one head of a larger problem can be evaluated on its own (it has no
+    other effect).
     """
     B, H, N, _ = q.shape
     o = np.zeros((B, H, N, v.shape[-1]), np.float64)
@@ -156,7 +159,8 @@ def forward(q, k, v, scale, *, causal=False, key_lens=None, block_mask=None,
                 rows = np.arange(r0, min(N, r0 + chunk))
                 ob, lb = forward_rows(q[b, h], k[b, h], v[b, h], scale, rows,
                                       causal=causal, key_len=lens[b],
-                                      block_mask=bm, mb=mb, dropout=dropout, bh=b * H + h)
+                                      block_mask=bm, mb=mb, dropout=dropout,
+                                      bh=bh_offset + b * H + h)
                 o[b, h, rows] = ob
                 lse[b, h, rows] = lb
     return o, lse
@@ -179,12 +183,13 @@ def probabilities(q, k, scale, *, causal=False, key_len=None, block_mask=None, m
 
 
 def backward(q, k, v, do, scale, *, causal=False, key_lens=None, block_mask=None,
-             mb=128, chunk=1024, return_aux=False, dropout=None):
+             mb=128, chunk=1024, return_aux=False, dropout=None, bh_offset=0):
     """Analytic gradients of <dO, O> w.r.t. Q, K, V (fp64).
 
     Returns (dq, dk, dv); with ``return_aux`` also (o, lse, D_from_p, D_from_o),
     where D_from_p = rowsum(P * dP) and D_from_o = rowsum(dO * O) -- equal in
-    exact arithmetic; the GPU computes the latter.
+    exact arithmetic; the GPU computes the latter.  ``bh_offset``: as for
+    :func:`forward` (dropout head index only).
     """
     B, H, N, d = q.shape
     Nk = k.shape[2]
@@ -208,7 +213,7 @@ def backward(q, k, v, do, scale, *, causal=False, key_lens=None, block_mask=None
                 s = np.where(a, s, -np.inf)
                 m, l, valid, e = _row_softmax_stats(s)
                 p = np.where(valid[:, None], e / np.where(valid, l, 1.0)[:, None], 0.0)
-                z = _z(b * H + h, rows, np.arange(Nk), dropout)
+                z = _z(bh_offset + b * H + h, rows, np.arange(Nk), dropout)
                 pz = p if z is None else p * z
                 oc = pz @ vb
                 dpc = dob[rows] @ vb.T
