@@ -7,12 +7,16 @@ through fa_bwd_ex, all on torch's current stream.  Prints ONE JSON line on stdou
   value      whole-step TFLOP/s, FLOPs counted as 4*B*H*N^2*d for the forward
              (halved when causal) and 2.5x that for the backward, over the
              wall-clock time of the timed steps (inputs resident in HBM).
+             Workloads with key padding or a block mask count 4d per visible
+             (query, key) pair instead (and also report the dense-equivalent
+             rate, labelled as such).
   roofline   the kernel with the largest average duration: algorithmic FLOPs
              of one launch over its average duration from HIP events recorded
              on the launch stream around every timed launch; per visible
              (query, key) pair: forward 4d (S, PV), backward dK/dV kernel 8d
-             (S, dP, dV, dK), backward dQ kernel 6d (S, dP, dQ; S and dP are
-             recomputed there); peak = dense bf16/fp16 MFMA 2516.6 TFLOP/s.  `traffic` comes from the
+             (S, dP, dV, dK), backward dQ kernel 2d (dQ; it also recomputes S
+             and dP, 4d more, reported apart as executed MFMA work); peak =
+             dense bf16/fp16 MFMA 2516.6 TFLOP/s.  `traffic` comes from the
              committed rocprofv3 counter summary when it was taken on the
              current kernel sources, else null.
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
@@ -99,12 +103,26 @@ def visible_pairs(w, key_lens=None, block_mask=None) -> int:
     return total
 
 
+def headline_count(w) -> bool:
+    """Whether the metric's own FLOP count applies: a square problem whose
+    only mask is (optionally) causal."""
+    return w.N == w.Nk and w.lens is None and w.mb is None
+
+
 def forward_flops(w, pairs) -> float:
-    """Headline forward FLOP count: 4 B H N^2 d (halved when causal) for a
-    square problem, 4 d per visible pair otherwise."""
-    if w.N == w.Nk:
+    """Forward FLOPs of one step: the metric's 4 B H N^2 d (halved when
+    causal) for a square dense or causal problem; 4 d per visible (query, key)
+    pair whenever padding, a block mask or N_q != N_k removes pairs (the
+    dense count would credit work that is never done)."""
+    if headline_count(w):
         return 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
     return 4.0 * w.d * pairs
+
+
+def dense_equivalent_flops(w) -> float:
+    """4 B H N_q N_k d (halved when causal): what the same shape would cost
+    with no mask, for context on masked workloads only."""
+    return 4.0 * w.B * w.H * w.N * w.Nk * w.d * (0.5 if w.causal else 1.0)
 
 
 def traffic_from_profile(workload: str, kernel: str):
@@ -560,15 +578,23 @@ def main():
     f_fwd = forward_flops(w, pairs)
     f_step = 3.5 * f_fwd
     value = f_step / (ms_step * 1e-3) / 1e12
+    # Algorithmic FLOPs per visible pair (the method's own matrix work): the
+    # forward's S and PV (4d); the dK/dV kernel's S, dP, dV, dK (8d); the dQ
+    # kernel's dQ product (2d).  The dQ kernel also recomputes S and dP (4d
+    # more per pair, executed MFMA work but not the method's): reported apart.
     kernels = {
-        "fwd_kernel": (fwd_ms, 4.0 * w.d * pairs),
-        "bwd_main_kernel": (main_ms, 8.0 * w.d * pairs),
-        "bwd_dq_kernel": (dq_ms, 6.0 * w.d * pairs),
+        "fwd_kernel": (fwd_ms, 4.0 * w.d * pairs, 4.0 * w.d * pairs),
+        "bwd_main_kernel": (main_ms, 8.0 * w.d * pairs, 8.0 * w.d * pairs),
+        "bwd_dq_kernel": (dq_ms, 2.0 * w.d * pairs, 6.0 * w.d * pairs),
     }
     name = max(kernels, key=lambda n: kernels[n][0])
-    dur_ms, alg_flops = kernels[name]
+    dur_ms, alg_flops, _ = kernels[name]
     achieved = alg_flops / (dur_ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
+    alg_step = 14.0 * w.d * pairs  # forward 4d + backward 10d per visible pair
+    kernel_tflops = {n: {"algorithmic": round(a / (t * 1e-3) / 1e12, 1),
+                         "executed_mfma": round(x / (t * 1e-3) / 1e12, 1)}
+                     for n, (t, a, x) in kernels.items()}
     label = w.name if args.dropout == 0.0 else f"{w.name}_dropout{args.dropout:g}"
     traffic = traffic_from_profile(label, name)
 
@@ -588,9 +614,16 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_k": w.Nk, "d": w.d,
                    "causal": w.causal, "mask_block": w.mb, "key_padding": w.lens is not None,
                    "dropout": args.dropout},
+        "flop_count": ("4 B H N^2 d (halved when causal); backward 2.5x" if headline_count(w)
+                       else "4 d per visible (query, key) pair; backward 2.5x"),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
         "bwd_tflops": round(2.5 * f_fwd / ((pre_ms + main_ms + dq_ms) * 1e-3) / 1e12, 3),
-        "mfma_peak_frac_step": round(value / peak, 4),
+        "mfma_peak_frac_step": round(alg_step / (ms_step * 1e-3) / 1e12 / peak, 4),
+        "bwd_algorithmic_frac": round(10.0 * w.d * pairs / ((pre_ms + main_ms + dq_ms) * 1e-3)
+                                      / 1e12 / peak, 4),
+        "kernel_tflops": kernel_tflops,
+        **({} if headline_count(w) else {"dense_equivalent_tflops": round(
+            3.5 * dense_equivalent_flops(w) / (ms_step * 1e-3) / 1e12, 1)}),
         "warmup_extra_steps": time_attention.extra_warmup,
         **({"graph_ms_per_step": round(time_attention.graph_ms, 4),
             "graph_tflops": round(f_step / (time_attention.graph_ms * 1e-3) / 1e12, 3),

@@ -27,6 +27,7 @@ from ._lib import FaError, FaProblem
 
 __all__ = ["fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
            "fa_fwd_splitkv_workspace_bytes", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_ex",
+           "fa_merge_partials",
            "fa_bwd_workspace_bytes", "fa_softmax_rows", "fa_layernorm_rows", "fa_group_norm",
            "FaError", "library_path", "load_library",
            "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_DQ", "FA_BWD_ALL"]
@@ -93,6 +94,29 @@ def _same_layout(ref, *others):
                              "and device")
 
 
+def _stats(t, shape, like, name, required=False):
+    """A float32 per-row array (LSE, mean, rstd) of the given shape, new when
+    ``t`` is None.  The library reads or writes prod(shape) contiguous floats
+    through the bare pointer, so a caller's tensor must hold exactly that, on
+    the device of ``like``."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return torch.empty(shape, dtype=torch.float32, device=like.device)
+    n = math.prod(shape)
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n or t.device != like.device:
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements on {like.device}")
+    return t
+
+
+def _workspace(ws, need, like):
+    if ws is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=like.device)
+    if ws.device != like.device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {like.device}")
+    return ws
+
+
 def _empty_like_layout(q):
     return torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
 
@@ -103,7 +127,7 @@ def fa_fwd(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=No
     _same_layout(k, v)
     p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
     o = _empty_like_layout(q) if out is None else out
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    lse = _stats(lse, tuple(q.shape[:3]), q, "lse")
     _same_layout(q, o)
     lib = _lib.load()
     _lib.check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(q)))
@@ -119,7 +143,7 @@ def fa_fwd_blocksparse(q, k, v, block_mask, *, mask_block=128, scale=None, causa
     p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
     bm, hstride = _mask(block_mask, q, k, mask_block)
     o = _empty_like_layout(q) if out is None else out
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    lse = _stats(lse, tuple(q.shape[:3]), q, "lse")
     _same_layout(q, o)
     lib = _lib.load()
     _lib.check(lib.fa_fwd_blocksparse(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
@@ -142,6 +166,32 @@ def _mask(block_mask, q, k, mask_block):
     if bm.dim() == 3 and bm.shape[0] == q.shape[1] and (want is None or tuple(bm.shape[1:]) == want):
         return bm, bm.stride(0)
     raise ValueError(f"block_mask must be [N_q/mb, N_k/mb] = {want} or [H, N_q/mb, N_k/mb]")
+
+
+def fa_merge_partials(o_parts, lse_parts, *, out=None, lse=None):
+    """Merge partial results (O_s, LSE_s) computed over disjoint key sets into
+    (O, LSE): LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+    ``o_parts``: sequence of S [B, H, N_q, d] tensors sharing one layout;
+    ``lse_parts``: S float32 [B, H, N_q] tensors.  ``out`` / ``lse`` may be
+    one of the parts (in-place).  Calls fa_merge_partials."""
+    o_parts, lse_parts = list(o_parts), list(lse_parts)
+    S = len(o_parts)
+    if S < 1 or S != len(lse_parts) or S > _lib.FA_MERGE_MAX_PARTS:
+        raise ValueError(f"need 1..{_lib.FA_MERGE_MAX_PARTS} O parts and as many LSE parts")
+    ref = o_parts[0]
+    _same_layout(ref, *o_parts[1:])
+    shape = tuple(ref.shape[:3])
+    for t in lse_parts:
+        _stats(t, shape, ref, "each LSE part", required=True)
+    o = _empty_like_layout(ref) if out is None else out
+    _same_layout(ref, o)
+    lse = _stats(lse, shape, ref, "lse")
+    p, _ = _problem(ref, ref, 1.0, False, None)
+    optr = (ctypes.c_void_p * S)(*[t.data_ptr() for t in o_parts])
+    lptr = (ctypes.c_void_p * S)(*[t.data_ptr() for t in lse_parts])
+    lib = _lib.load()
+    _lib.check(lib.fa_merge_partials(ctypes.byref(p), S, optr, lptr, _ptr(o), _ptr(lse), _stream(ref)))
+    return o, lse
 
 
 def fa_fwd_splitkv_num_splits(q, k, *, scale=None, causal=False, key_lens=None) -> int:
@@ -173,12 +223,10 @@ def fa_fwd_splitkv(q, k, v, *, num_splits=0, block_mask=None, mask_block=128, sc
     p, kl = _problem(q, k, scale, causal, key_lens)
     bm, hstride = (None, 0) if block_mask is None else _mask(block_mask, q, k, mask_block)
     o = _empty_like_layout(q) if out is None else out
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    lse = _stats(lse, tuple(q.shape[:3]), q, "lse")
     _same_layout(q, o)
     lib = _lib.load()
-    if workspace is None:
-        need = lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), int(num_splits))
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), int(num_splits)), q)
     _lib.check(lib.fa_fwd_splitkv(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
                                   int(num_splits), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -199,9 +247,7 @@ def fa_bwd_workspace_bytes(q, k=None, *, scale=None, causal=False, key_lens=None
 
 def _bwd_outputs(q, k, workspace, p, grads):
     lib = _lib.load()
-    need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, lib.fa_bwd_workspace_bytes(ctypes.byref(p)), q)
     outs = []
     for like, g in zip((q, k, k), grads):
         if g is None:
@@ -218,6 +264,7 @@ def fa_bwd(q, k, v, o, lse, do, *, scale=None, causal=False, key_lens=None, work
     _same_layout(q, o, do)
     _same_layout(k, v)
     p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    _stats(lse, tuple(q.shape[:3]), q, "lse", required=True)
     dq, dk, dv, ws = _bwd_outputs(q, k, workspace, p, (dq, dk, dv))
     lib = _lib.load()
     _lib.check(lib.fa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
@@ -233,6 +280,7 @@ def fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, *, mask_block=128, scale
     _same_layout(q, o, do)
     _same_layout(k, v)
     p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    _stats(lse, tuple(q.shape[:3]), q, "lse", required=True)
     bm, hstride = _mask(block_mask, q, k, mask_block)
     dq, dk, dv, ws = _bwd_outputs(q, k, workspace, p, (dq, dk, dv))
     lib = _lib.load()
@@ -252,8 +300,10 @@ def fa_bwd_ex(q, k, v, o, lse, do, stages, *, block_mask=None, mask_block=128, s
     _same_layout(q, o, do, dq)
     _same_layout(k, v, dk, dv)
     p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    _stats(lse, tuple(q.shape[:3]), q, "lse", required=True)
     bm, hstride = (None, 0) if block_mask is None else _mask(block_mask, q, k, mask_block)
     lib = _lib.load()
+    workspace = _workspace(workspace, 0, q)
     _lib.check(lib.fa_bwd_ex(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
                              _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
@@ -276,7 +326,7 @@ def fa_softmax_rows(x, *, out=None, lse=None):
     _, _, ldy = _rows_view(y)
     if y.shape != x.shape or y.dtype != x.dtype:
         raise ValueError("out must match x in shape and dtype")
-    lse = torch.empty(rows, dtype=torch.float32, device=x.device) if lse is None else lse
+    lse = _stats(lse, (rows,), x, "lse")
     lib = _lib.load()
     _lib.check(lib.fa_softmax_rows(_DTYPES[x.dtype], rows, cols, _ptr(x), ld, _ptr(y), ldy, _ptr(lse),
                                    _stream(x)))
@@ -296,8 +346,8 @@ def fa_layernorm_rows(x, gamma=None, beta=None, *, eps=1e-5, groups=1, inner=1, 
     for t in (gamma, beta):
         if t is not None and (t.dtype != x.dtype or t.numel() != nch or not t.is_contiguous()):
             raise ValueError(f"gamma / beta must be contiguous {x.dtype} of {nch} channels")
-    mean = torch.empty(rows, dtype=torch.float32, device=x.device) if mean is None else mean
-    rstd = torch.empty(rows, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    mean = _stats(mean, (rows,), x, "mean")
+    rstd = _stats(rstd, (rows,), x, "rstd")
     lib = _lib.load()
     _lib.check(lib.fa_layernorm_rows(_DTYPES[x.dtype], rows, cols, _ptr(x), ld, _ptr(gamma), _ptr(beta),
                                      float(eps), int(groups), int(inner), _ptr(y), ldy, _ptr(mean),

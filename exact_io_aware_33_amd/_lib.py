@@ -11,11 +11,13 @@ FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
+           "fa_merge_partials",
            "fa_fwd_splitkv_workspace_bytes", "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_bwd_blocksparse", "fa_bwd_ex", "fa_softmax_rows", "fa_layernorm_rows",
            "fa_status_string", "fa_last_error", "fa_abi_version")
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
-ABI_VERSION = 3
+FA_MERGE_MAX_PARTS = 64
+ABI_VERSION = 4
 
 
 class FaProblem(ctypes.Structure):
@@ -74,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_splitkv_num_splits.restype = i32
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [pp, i32]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
+    lib.fa_merge_partials.argtypes = [pp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
+    lib.fa_merge_partials.restype = i32
     lib.fa_bwd_workspace_bytes.argtypes = [pp]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]

@@ -26,6 +26,11 @@ fa_status_t fail(fa_status_t st, const char *fmt, ...) {
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+// Rows past the end of a (batch, head) slice that a tile may address (the
+// largest tile is 128 rows); they read as zeros through the buffer range
+// check.
+constexpr int64_t kRowSlack = 256;
+
 int elem_size(int32_t dt) { return dt == FA_DTYPE_F32 ? 4 : 2; }
 
 int32_t keys_of(const fa_problem_t *p) { return p->seqlen_k ? p->seqlen_k : p->seqlen; }
@@ -54,19 +59,31 @@ fa_status_t check_problem(const fa_problem_t *p) {
     if (bh * n * p->head_dim >= (int64_t(1) << 31))
       return fail(FA_ERR_UNSUPPORTED, "B*H*N*d exceeds the 32-bit index range");
   const int es = elem_size(p->dtype);
+  const bool kdef = k_strides_default(p);
   const int64_t st[2][3] = {{p->stride_b, p->stride_h, p->stride_n},
-                            {p->k_stride_b, p->k_stride_h, p->k_stride_n}};
-  for (int t = 0; t < (k_strides_default(p) ? 1 : 2); ++t) {
+                            {kdef ? p->stride_b : p->k_stride_b, kdef ? p->stride_h : p->k_stride_h,
+                             kdef ? p->stride_n : p->k_stride_n}};
+  const int64_t rows_of[2] = {p->seqlen, keys_of(p)};
+  for (int t = 0; t < 2; ++t) {
+    const char *nm = t ? "k_stride_n" : "stride_n";
     if (st[t][0] < 0 || st[t][1] < 0 || st[t][2] < 0)
       return fail(FA_ERR_INVALID, "strides must be non-negative");
-    if ((st[t][0] * es) % 16 || (st[t][1] * es) % 16 || (st[t][2] * es) % 16)
-      return fail(FA_ERR_INVALID, "strides must be multiples of 16 bytes");
     if (st[t][2] < p->head_dim)
-      return fail(FA_ERR_INVALID, "%s (%lld) smaller than head_dim", t ? "k_stride_n" : "stride_n",
-                  (long long)st[t][2]);
+      return fail(FA_ERR_INVALID, "%s (%lld) smaller than head_dim", nm, (long long)st[t][2]);
+    if ((st[t][0] * es) % 16 || (st[t][1] * es) % 16 || (st[t][2] * es) % 16)
+      return fail(FA_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes (16-byte vector path)");
+    // The kernels address the rows of one (batch, head) slice -- including
+    // up to kRowSlack rows past its end, which a tile may overrun and the
+    // buffer range check turns into zeros -- with 32-bit byte offsets from
+    // the slice's start (buffer record count, tile offsets).
+    if ((rows_of[t] + kRowSlack) * st[t][2] * es >= (int64_t(1) << 31))
+      return fail(FA_ERR_UNSUPPORTED,
+                  "(%s + %d) * %s * element size = %lld bytes reaches 2^31 (32-bit row offsets)",
+                  t ? "N_k" : "N_q", (int)kRowSlack, nm,
+                  (long long)((rows_of[t] + kRowSlack) * st[t][2] * es));
   }
   if (p->key_lens && !aligned16(p->key_lens))
-    return fail(FA_ERR_INVALID, "key_lens must be 16-byte aligned");
+    return fail(FA_ERR_UNSUPPORTED, "key_lens must be 16-byte aligned");
   if (!std::isfinite(p->dropout_p) || p->dropout_p < 0.f || p->dropout_p >= 1.f)
     return fail(FA_ERR_INVALID, "dropout_p must be in [0, 1)");
   return FA_OK;
@@ -81,7 +98,8 @@ uint32_t drop_threshold(float p) {
 
 fa_status_t check_tensor(const void *ptr, const char *name) {
   if (!ptr) return fail(FA_ERR_INVALID, "%s is NULL", name);
-  if (!aligned16(ptr)) return fail(FA_ERR_INVALID, "%s is not 16-byte aligned", name);
+  if (!aligned16(ptr))
+    return fail(FA_ERR_UNSUPPORTED, "%s is not 16-byte aligned (16-byte vector path)", name);
   return FA_OK;
 }
 
@@ -172,10 +190,25 @@ int32_t auto_splits(const fa_problem_t *p) {
   return (int32_t)std::max<int64_t>(1, sp);
 }
 
+}  // namespace
+
+namespace fa {
+
+fa_status_t set_error(fa_status_t st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+// The backward entry points.  With `scratch` set, the workspace is not an
+// argument: once every argument has passed its checks, scratch(need, &ws,
+// &ws_bytes) supplies it (and may refuse).
 fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int64_t hstride,
                      bool sparse, const void *q, const void *k, const void *v, const void *o,
                      const float *lse, const void *dout, void *dq, void *dk, void *dv, void *ws,
-                     size_t ws_bytes, unsigned stages, void *stream) {
+                     size_t ws_bytes, unsigned stages, void *stream, ScratchFn scratch) {
   g_err[0] = 0;
   if (stages == 0 || (stages & ~(unsigned)FA_BWD_ALL))
     return fail(FA_ERR_INVALID, "stages must be a nonzero subset of FA_BWD_ALL (got %u)", stages);
@@ -185,11 +218,13 @@ fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
       (st = check_tensor(v, "v")) != FA_OK || (st = check_tensor(o, "o")) != FA_OK ||
       (st = check_tensor(lse, "lse")) != FA_OK || (st = check_tensor(dout, "dout")) != FA_OK ||
       (st = check_tensor(dq, "dq")) != FA_OK || (st = check_tensor(dk, "dk")) != FA_OK ||
-      (st = check_tensor(dv, "dv")) != FA_OK || (st = check_tensor(ws, "workspace")) != FA_OK)
+      (st = check_tensor(dv, "dv")) != FA_OK)
     return st;
+  if (!scratch && (st = check_tensor(ws, "workspace")) != FA_OK) return st;
   if (sparse && (st = check_mask(p, mask, mb, hstride)) != FA_OK) return st;
   const int64_t rows = (int64_t)p->batch * p->heads * p->seqlen;
   const size_t need = fa::ws_total_bytes(rows);
+  if (scratch && (st = scratch(need, &ws, &ws_bytes)) != FA_OK) return st;
   if (ws_bytes < need)
     return fail(FA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
   fa::AttnParams a = make_params(p);
@@ -214,7 +249,9 @@ fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
   return hip_status(fa::launch_bwd(a, (fa_dtype_t)p->dtype, sparse, stages, (hipStream_t)stream));
 }
 
-}  // namespace
+}  // namespace fa
+
+using fa::bwd_impl;
 
 extern "C" {
 
@@ -240,7 +277,7 @@ fa_status_t fa_bwd(const fa_problem_t *p, const void *q, const void *k, const vo
                    const float *lse, const void *dout, void *dq, void *dk, void *dv, void *workspace,
                    size_t workspace_bytes, void *stream) {
   return bwd_impl(p, nullptr, 0, 0, false, q, k, v, o, lse, dout, dq, dk, dv, workspace,
-                  workspace_bytes, FA_BWD_ALL, stream);
+                  workspace_bytes, FA_BWD_ALL, stream, nullptr);
 }
 
 fa_status_t fa_bwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask, int32_t mask_block,
@@ -248,7 +285,7 @@ fa_status_t fa_bwd_blocksparse(const fa_problem_t *p, const uint8_t *block_mask,
                                const void *o, const float *lse, const void *dout, void *dq, void *dk,
                                void *dv, void *workspace, size_t workspace_bytes, void *stream) {
   return bwd_impl(p, block_mask, mask_block, mask_head_stride, true, q, k, v, o, lse, dout, dq, dk, dv,
-                  workspace, workspace_bytes, FA_BWD_ALL, stream);
+                  workspace, workspace_bytes, FA_BWD_ALL, stream, nullptr);
 }
 
 fa_status_t fa_bwd_ex(const fa_problem_t *p, const uint8_t *block_mask, int32_t mask_block,
@@ -256,7 +293,39 @@ fa_status_t fa_bwd_ex(const fa_problem_t *p, const uint8_t *block_mask, int32_t 
                       const void *o, const float *lse, const void *dout, void *dq, void *dk, void *dv,
                       void *workspace, size_t workspace_bytes, uint32_t stages, void *stream) {
   return bwd_impl(p, block_mask, mask_block, mask_head_stride, block_mask != nullptr, q, k, v, o, lse,
-                  dout, dq, dk, dv, workspace, workspace_bytes, stages, stream);
+                  dout, dq, dk, dv, workspace, workspace_bytes, stages, stream, nullptr);
+}
+
+fa_status_t fa_merge_partials(const fa_problem_t *p, int32_t num_parts, const void *const *o_parts,
+                              const float *const *lse_parts, void *o, float *lse, void *stream) {
+  g_err[0] = 0;
+  fa_status_t st;
+  if ((st = check_problem(p)) != FA_OK) return st;
+  if (num_parts < 1 || num_parts > FA_MERGE_MAX_PARTS)
+    return fail(FA_ERR_INVALID, "num_parts must be in [1, %d] (got %d)", FA_MERGE_MAX_PARTS, num_parts);
+  if (!o_parts || !lse_parts) return fail(FA_ERR_INVALID, "o_parts and lse_parts must not be NULL");
+  fa::MergeParams a{};
+  for (int s = 0; s < num_parts; ++s) {
+    char name[32];
+    snprintf(name, sizeof name, "o_parts[%d]", s);
+    if ((st = check_tensor(o_parts[s], name)) != FA_OK) return st;
+    snprintf(name, sizeof name, "lse_parts[%d]", s);
+    if ((st = check_tensor(lse_parts[s], name)) != FA_OK) return st;
+    a.o_parts[s] = o_parts[s];
+    a.lse_parts[s] = lse_parts[s];
+  }
+  if ((st = check_tensor(o, "o")) != FA_OK || (st = check_tensor(lse, "lse")) != FA_OK) return st;
+  a.o = o;
+  a.lse = lse;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.Nq = p->seqlen;
+  a.d = p->head_dim;
+  a.S = num_parts;
+  a.sb = p->stride_b;
+  a.sh = p->stride_h;
+  a.sn = p->stride_n;
+  return hip_status(fa::launch_merge(a, (fa_dtype_t)p->dtype, (hipStream_t)stream));
 }
 
 int32_t fa_fwd_splitkv_num_splits(const fa_problem_t *p) {

@@ -48,6 +48,18 @@ struct AttnParams {
   float *part_lse;           // [nsplit][B*H*N_q]
 };
 
+// Merge of partial results over disjoint key sets (fa_merge.hip): part s is
+// (o_parts[s], lse_parts[s]); O and every O_s share the strides (sb, sh, sn).
+struct MergeParams {
+  const void *o_parts[FA_MERGE_MAX_PARTS];
+  const float *lse_parts[FA_MERGE_MAX_PARTS];
+  void *o;
+  float *lse;
+  int32_t B, H, Nq, d, S;
+  int64_t sb, sh, sn;
+};
+hipError_t launch_merge(const MergeParams &p, fa_dtype_t dt, hipStream_t s);
+
 // Row reductions (fa_reduce.hip): softmax, LayerNorm / GroupNorm.
 struct RedParams {
   const void *x;
@@ -74,6 +86,22 @@ int fwd_key_tile(fa_dtype_t dt);
 // `stages`: bit set of FA_BWD_PRE / FA_BWD_MAIN / FA_BWD_DQ, run in that order.
 hipError_t launch_bwd(const AttnParams &p, fa_dtype_t dt, bool sparse, unsigned stages,
                       hipStream_t s);
+
+// Records a message for fa_last_error() and returns `st`.
+fa_status_t set_error(fa_status_t st, const char *fmt, ...);
+
+// Supplies the backward workspace of at least `need` bytes when the caller
+// passes none (the allocation-free entry point): sets *ws and *bytes or
+// returns an error status (with set_error).
+typedef fa_status_t (*ScratchFn)(size_t need, void **ws, size_t *bytes);
+
+// Argument checks and the backward launch sequence shared by every backward
+// entry point (fa_api.cpp).  With `scratch` non-null, `ws` / `ws_bytes` are
+// ignored and the workspace comes from scratch() after all other checks.
+fa_status_t bwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int64_t hstride,
+                     bool sparse, const void *q, const void *k, const void *v, const void *o,
+                     const float *lse, const void *dout, void *dq, void *dk, void *dv, void *ws,
+                     size_t ws_bytes, unsigned stages, void *stream, ScratchFn scratch);
 
 // Backward workspace: two floats per query row, each array 256-byte aligned:
 // -D = -rowsum(dO * O), then LSE in the base-2 domain.

@@ -64,7 +64,8 @@
  *   and keeps every buffer alive until then.
  * Alignment.  Q, K, V, O, dO, dQ, dK, dV must be 16-byte aligned and all six
  *   strides multiples of 16 bytes; LSE, key_lens and the workspace 16-byte
- *   aligned.
+ *   aligned (the kernels move 16-byte vectors).  A NULL pointer is
+ *   FA_ERR_INVALID; a misaligned pointer or stride is FA_ERR_UNSUPPORTED.
  * Errors.  Argument errors are detected on the host before any HIP call and
  *   returned synchronously (FA_ERR_INVALID, FA_ERR_UNSUPPORTED); a failed
  *   launch returns FA_ERR_HIP.  Faults during execution surface at the
@@ -74,7 +75,13 @@
  * Supported shapes.  dtype FP16 or BF16 with d in {64, 128}; dtype FP32 with
  *   d in {64, 128}.  N_q, N_k >= 1 (any values, not only multiples of the
  *   tile), B >= 1, H >= 1, B*H*N*d < 2^31 for N = N_q and N = N_k.  scale
- *   finite and >= 0.
+ *   finite and >= 0.  The kernels address the rows of one (batch, head)
+ *   slice with 32-bit byte offsets from its first row, tiles overrunning the
+ *   end by up to 256 rows (read as zeros), so
+ *       (N_q + 256) * stride_n * element size   < 2^31  and
+ *       (N_k + 256) * k_stride_n * element size < 2^31
+ *   (FA_ERR_UNSUPPORTED otherwise; e.g. [B, N, H, d] storage with
+ *   N * H * d * element size near 2 GiB).
  */
 #ifndef EXACT_IO_AWARE_FA_H
 #define EXACT_IO_AWARE_FA_H
@@ -86,7 +93,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum fa_dtype {
   FA_DTYPE_F32 = 0,   /* IEEE float32 storage, float32 arithmetic            */
@@ -99,11 +106,12 @@ typedef enum fa_status {
   FA_ERR_INVALID = 1,      /* bad argument: NULL pointer, size <= 0, non-finite
                               or negative scale, dropout_p outside [0, 1),
                               workspace too small, block size that does not
-                              divide N_q and N_k, misaligned pointer, nonzero
-                              reserved field                                 */
+                              divide N_q and N_k, row stride below head_dim,
+                              nonzero reserved field                         */
   FA_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim / dtype pair,
-                              block size not a multiple of 128, sizes over the
-                              32-bit index range                              */
+                              block size not a multiple of 128, a pointer or
+                              stride that is not 16-byte aligned, sizes over
+                              the 32-bit index / byte-offset ranges           */
   FA_ERR_HIP = 3           /* the HIP runtime refused a launch                 */
 } fa_status_t;
 
@@ -189,6 +197,38 @@ fa_status_t fa_fwd_splitkv(const fa_problem_t *p, const uint8_t *block_mask, int
                            int64_t mask_head_stride, int32_t num_splits, const void *q,
                            const void *k, const void *v, void *o, float *lse, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* Merge of partial results over disjoint key sets (summary page, section
+ * "Incremental softmax tracking": the merge equation, here in log-sum-exp
+ * form, since each part's output is already divided by its own sum):
+ *     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * Part s is what fa_fwd / fa_fwd_blocksparse return for the queries against
+ * the s-th of S disjoint subsets of the keys -- the per-hop result of
+ * context-parallel (ring) attention, where K / V shards visit each query
+ * shard in turn (same page, "Limitations and open questions": attention
+ * across devices is left open there).  The merged (O, LSE) is the forward
+ * result over the union of the key sets, and is what fa_bwd needs, per
+ * shard, for that shard's exact dK, dV and its share of dQ (the shares sum
+ * to dQ).
+ *   p          : the problem of the queries; batch, heads, seqlen (N_q),
+ *                head_dim, stride_b / _h / _n and dtype are used (all other
+ *                fields are checked as for fa_fwd and otherwise ignored).
+ *   num_parts  : S, 1 <= S <= FA_MERGE_MAX_PARTS.
+ *   o_parts    : HOST array of S device pointers; o_parts[s] is an
+ *                [B,H,N_q,d] array of dtype with p's strides (read only).
+ *   lse_parts  : HOST array of S device pointers; lse_parts[s] is a
+ *                contiguous float32 [B,H,N_q] array (read only).  A part with
+ *                LSE_s = -inf (it saw no key) weighs 0, whatever its O_s.
+ *   o, lse     : outputs, laid out as the parts; o may be the same memory as
+ *                any o_parts[s], lse as any lse_parts[s] (in-place merge).
+ *                A row no part saw gets O = 0, LSE = -inf.
+ * Arithmetic in fp32; O is rounded to dtype once.  Nothing is allocated:
+ * the S pointers travel in the kernel's arguments. */
+#define FA_MERGE_MAX_PARTS 64
+fa_status_t fa_merge_partials(const fa_problem_t *p, int32_t num_parts,
+                              const void *const *o_parts,
+                              const float *const *lse_parts, void *o,
+                              float *lse, void *stream);
 
 /* Size in bytes of the device workspace fa_bwd needs for problem p (0 if p is
  * invalid).  It holds two float32 per query row (B*H*N_q rows): rowsum(dO * O)

@@ -53,7 +53,7 @@ def test_exports_match_header(lib):
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fa_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.fa_abi_version() == _lib.ABI_VERSION == 4
 
 
 def test_status_strings(lib):
@@ -67,7 +67,9 @@ def test_status_strings(lib):
     ("head_dim", 0, INVALID), ("head_dim", 96, UNSUPPORTED), ("head_dim", 256, UNSUPPORTED),
     ("dtype", 7, INVALID), ("scale", float("nan"), INVALID), ("scale", float("inf"), INVALID),
     ("scale", -0.5, INVALID), ("stride_n", 60, INVALID), ("stride_n", 36, INVALID),
-    ("stride_h", -64, INVALID), ("key_lens", 0x10004, INVALID),
+    ("stride_h", -64, INVALID), ("key_lens", 0x10004, UNSUPPORTED),
+    ("stride_b", 4, UNSUPPORTED), ("stride_h", 3 * 256 * 64 + 4, UNSUPPORTED),
+    ("stride_n", 68, UNSUPPORTED),
     ("seqlen", 1 << 30, UNSUPPORTED),
     ("dropout_p", -0.1, INVALID), ("dropout_p", 1.0, INVALID), ("dropout_p", 1.5, INVALID),
     ("dropout_p", float("nan"), INVALID), ("dropout_p", float("inf"), INVALID),
@@ -87,17 +89,19 @@ def test_null_problem(lib):
 
 
 @pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
-@pytest.mark.parametrize("bad", [0, A + 8])
-def test_forward_pointers(lib, which, bad):
+@pytest.mark.parametrize("bad,status", [(0, INVALID), (A + 8, UNSUPPORTED)])
+def test_forward_pointers(lib, which, bad, status):
+    """NULL is an invalid argument; a pointer off the 16-byte grid is a
+    layout the vector path is not built for."""
     kw = {which: bad}
-    assert fwd(lib, prob(), **kw) == INVALID
+    assert fwd(lib, prob(), **kw) == status
     assert which in lib.fa_last_error().decode()
 
 
 @pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"])
 def test_backward_pointers(lib, which):
     assert bwd(lib, prob(), **{which: 0}) == INVALID
-    assert bwd(lib, prob(), **{which: A + 4}) == INVALID
+    assert bwd(lib, prob(), **{which: A + 4}) == UNSUPPORTED
 
 
 def test_workspace_size_and_too_small(lib):
@@ -110,7 +114,49 @@ def test_workspace_size_and_too_small(lib):
 
 def test_fp32_strides_need_16_bytes(lib):
     p = prob(dtype=_lib.FA_DTYPE_F32, stride_n=66, stride_h=256 * 66, stride_b=3 * 256 * 66)
-    assert fwd(lib, p) == INVALID
+    assert fwd(lib, p) == UNSUPPORTED
+
+
+def _bnhd(N, H, d, **kw):
+    """[B=1, N, H, d] storage seen as [B, H, N, d]: stride_n = H d."""
+    return prob(batch=1, heads=H, seqlen=N, head_dim=d, stride_b=N * H * d, stride_h=d,
+                stride_n=H * d, **kw)
+
+
+@pytest.mark.parametrize("case", ["packed_qkv_bf16", "bnhd_fp32", "bnhd_keys_fp32"])
+def test_row_byte_offsets_over_31_bits_rejected(lib, case):
+    """The kernels address one (batch, head) slice's rows with 32-bit byte
+    offsets (buffer record count, tile offsets), tiles overrunning the end by
+    up to 256 rows: (N + 256) * stride_n * element size must stay below 2^31.
+    Layouts whose elements fit the 2^31 index bound can still break that."""
+    if case == "packed_qkv_bf16":
+        # [B, N, 3, H, d] bf16 packed QKV, H = 32, N = 512K: B*H*N*d = 2^30,
+        # but a slice spans (N - 1) * 6144 * 2 bytes ~ 6.4e9
+        N, H, d = 1 << 19, 32, 64
+        p = prob(batch=1, heads=H, seqlen=N, head_dim=d, stride_b=N * 3 * H * d, stride_h=d,
+                 stride_n=3 * H * d)
+    elif case == "bnhd_fp32":
+        p = _bnhd(1 << 20, 16, 64, dtype=_lib.FA_DTYPE_F32)        # 4 GiB slice span
+    else:
+        # queries small, keys in a [B, N_k, H, d] fp32 layout over 4 GiB
+        Nk, H, d = 131072, 127, 128
+        p = prob(batch=1, heads=H, seqlen=64, head_dim=d, stride_b=H * 64 * d, stride_h=64 * d,
+                 stride_n=d, dtype=_lib.FA_DTYPE_F32, seqlen_k=Nk, k_stride_b=Nk * H * d,
+                 k_stride_h=d, k_stride_n=H * d)
+    assert fwd(lib, p) == UNSUPPORTED
+    assert "2^31" in lib.fa_last_error().decode()
+    assert bwd(lib, p, ws_bytes=1 << 40) == UNSUPPORTED
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_row_byte_offsets_at_the_bound(lib):
+    """(N + 256) * stride_n * e just below 2^31 passes, at 2^31 fails."""
+    H, d = 16, 64                      # bf16 [1, N, 16, 64]: 2048 bytes per row
+    N_ok = (1 << 31) // 2048 - 256 - 1
+    # the argument checks alone (a passing fwd call would launch on these fake
+    # addresses): the workspace-size query runs exactly those checks
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(_bnhd(N_ok, H, d))) > 0
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(_bnhd(N_ok + 1, H, d))) == 0
 
 
 @pytest.mark.parametrize("mb,hstride,status", [
@@ -257,4 +303,39 @@ def test_layernorm_rows_rejected(lib, args, status):
     assert lib.fa_layernorm_rows(a["dtype"], a["rows"], a["cols"], a["x"], a["ld_x"], a["gamma"],
                                  a["beta"], a["eps"], a["groups"], a["inner"], a["y"], a["ld_y"],
                                  a["mean"], a["rstd"], None) == status
+    assert lib.fa_last_error()
+
+
+def _merge(lib, p, parts, lse_parts, o=A, lse=A, n=None):
+    S = len(parts) if n is None else n
+    op = None if parts is None else (ctypes.c_void_p * max(1, len(parts)))(*parts)
+    lp = None if lse_parts is None else (ctypes.c_void_p * max(1, len(lse_parts)))(*lse_parts)
+    return lib.fa_merge_partials(ctypes.byref(p), S, op, lp, o, lse, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("zero_parts", INVALID), ("too_many", INVALID), ("null_arrays", INVALID),
+    ("null_part", INVALID), ("misaligned_part", UNSUPPORTED), ("misaligned_lse_part", UNSUPPORTED),
+    ("null_out", INVALID), ("bad_problem", UNSUPPORTED),
+])
+def test_merge_rejected_before_any_hip_call(lib, case, status):
+    p = prob()
+    two = [A, A + 1024]
+    if case == "zero_parts":
+        st = _merge(lib, p, two, two, n=0)
+    elif case == "too_many":
+        st = _merge(lib, p, [A] * 65, [A] * 65)
+    elif case == "null_arrays":
+        st = _merge(lib, p, None, None, n=2)
+    elif case == "null_part":
+        st = _merge(lib, p, [A, 0], two)
+    elif case == "misaligned_part":
+        st = _merge(lib, p, [A, A + 8], two)
+    elif case == "misaligned_lse_part":
+        st = _merge(lib, p, two, [A, A + 4])
+    elif case == "null_out":
+        st = _merge(lib, p, two, two, o=0)
+    else:
+        st = _merge(lib, prob(head_dim=80), two, two)
+    assert st == status
     assert lib.fa_last_error()

@@ -162,6 +162,42 @@ def _sampled(w, heads, rows, cols):
     assert skd < 0.25
 
 
+def _full(w, *, row_blocks=False):
+    """Full-size launch; every element of every head against the oracle
+    (heads, or blocks of query rows, evaluated in parallel on the host)."""
+    from tests import _oracle_pool as pool
+
+    say(f"case {w.name} full size (N_q={w.N}, N_k={w.Nk}), every head against the oracle")
+    inp = make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed=0, mb=w.mb, density=w.density, n_keys=w.Nk)
+    dev = {n: inp[n].cuda() for n in ("q", "k", "v", "do")}
+    o, lse, (dq, dk, dv) = run(dev, w.scale, causal=w.causal, block_mask=inp["block_mask"], mb=w.mb or 128)
+    torch.cuda.synchronize()
+    got = (as_f64(o), lse.cpu().numpy(), as_f64(dq), as_f64(dk), as_f64(dv))
+    del dev, o, lse, dq, dk, dv
+    bm = None if w.mb is None else inp["block_mask"].numpy()
+    args = [as_f64(inp[n]) for n in ("q", "k", "v", "do")]
+    if row_blocks:
+        ref = pool.backward_row_blocks(*args, w.scale, causal=w.causal, block_mask=bm, mb=w.mb or 128)
+    else:
+        ref = pool.backward_all_heads(*args, w.scale, causal=w.causal, block_mask=bm, mb=w.mb or 128)
+    rdq, rdk, rdv, ro, rlse = ref
+    errs = {n: rel_err(g, r) for n, g, r in zip(("o", "lse", "dq", "dk", "dv"), got,
+                                                 (ro, rlse, rdq, rdk, rdv))}
+    say("  errors: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= TOL[w.dtype]}
+    assert not bad, f"over tolerance: {bad}"
+
+
+def test_workload_chunked_prefill_q4k_k16k_full():
+    _full(WORKLOADS["chunked_prefill_q4k_k16k"])
+
+
+def test_workload_blocksparse_n64k_full():
+    """64K queries and keys, 4 heads: the oracle splits each head into blocks
+    of 1024 query rows so that the host's cores share the work."""
+    _full(WORKLOADS["blocksparse_n64k"], row_blocks=True)
+
+
 def test_workload_chunked_prefill_q4k_k16k_sampled():
     w = WORKLOADS["chunked_prefill_q4k_k16k"]
     rng = np.random.default_rng(7)
