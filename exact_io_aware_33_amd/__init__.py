@@ -27,7 +27,7 @@ from ._lib import FaError, FaProblem
 
 __all__ = ["fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
            "fa_fwd_splitkv_workspace_bytes", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_ex",
-           "fa_merge_partials",
+           "fa_bwd_noalloc", "fa_merge_partials",
            "fa_bwd_workspace_bytes", "fa_softmax_rows", "fa_layernorm_rows", "fa_group_norm",
            "FaError", "library_path", "load_library",
            "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_DQ", "FA_BWD_ALL"]
@@ -308,6 +308,35 @@ def fa_bwd_ex(q, k, v, o, lse, do, stages, *, block_mask=None, mask_block=128, s
                              _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), int(stages), _stream(q)))
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, *, block_mask=None, mask_block=128, scale=None,
+                   causal=False, key_lens=None, dq=None, dk=None, dv=None, dropout_p=0.0,
+                   dropout_seed=0, dropout_offset=0):
+    """Gradients (dQ, dK, dV) with the library's static workspace instead of a
+    caller-supplied one (the entry point for callers that cannot allocate; at
+    most FA_BWD_NOALLOC_MAX_WORKSPACE_BYTES of workspace).  Calls
+    fa_bwd_noalloc on the device of q; block_mask None selects the dense path.
+    Gradient tensors the caller omits are allocated here, by torch, before
+    the call."""
+    _same_layout(q, o, do)
+    _same_layout(k, v)
+    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    _stats(lse, tuple(q.shape[:3]), q, "lse", required=True)
+    bm, hstride = (None, 0) if block_mask is None else _mask(block_mask, q, k, mask_block)
+    outs = []
+    for like, g in zip((q, k, k), (dq, dk, dv)):
+        if g is None:
+            g = _empty_like_layout(like)
+        else:
+            _same_layout(like, g)
+        outs.append(g)
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        _lib.check(lib.fa_bwd_noalloc(ctypes.byref(p), _ptr(bm), int(mask_block), int(hstride),
+                                      _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                      _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _stream(q)))
+    return outs[0], outs[1], outs[2]
 
 
 def _rows_view(x):

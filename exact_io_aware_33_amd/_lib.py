@@ -13,9 +13,10 @@ FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
            "fa_merge_partials",
            "fa_fwd_splitkv_workspace_bytes", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_bwd_blocksparse", "fa_bwd_ex", "fa_softmax_rows", "fa_layernorm_rows",
+           "fa_bwd_blocksparse", "fa_bwd_ex", "fa_bwd_noalloc", "fa_softmax_rows", "fa_layernorm_rows",
            "fa_status_string", "fa_last_error", "fa_abi_version")
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
+FA_BWD_NOALLOC_MAX_WORKSPACE_BYTES = 16 << 20
 FA_MERGE_MAX_PARTS = 64
 ABI_VERSION = 4
 
@@ -87,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_ex.argtypes = [pp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                               ctypes.c_uint32, vp]
     lib.fa_bwd_ex.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [pp, vp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fa_bwd_noalloc.restype = i32
     lib.fa_softmax_rows.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, vp]
     lib.fa_softmax_rows.restype = i32
     lib.fa_layernorm_rows.argtypes = [i32, i64, i64, vp, i64, vp, vp, ctypes.c_float, i32, i64, vp, i64,

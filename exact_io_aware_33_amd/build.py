@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_reduce.hip", "fa_merge.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_reduce.hip", "fa_merge.hip", "fa_api.cpp",
+           "fa_noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for every device compilation.

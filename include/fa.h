@@ -291,6 +291,33 @@ fa_status_t fa_bwd_ex(const fa_problem_t *p, const uint8_t *block_mask,
                       void *dq, void *dk, void *dv, void *workspace,
                       size_t workspace_bytes, uint32_t stages, void *stream);
 
+/* Allocation-free backward, for callers that cannot allocate device memory
+ * or be handed a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Computes exactly what fa_bwd_ex
+ * with FA_BWD_ALL computes (same kernels, same results; block_mask NULL = the
+ * dense path, otherwise as for fa_bwd_blocksparse), but its workspace is a
+ * fixed device array inside the library, of
+ * FA_BWD_NOALLOC_MAX_WORKSPACE_BYTES, which every GPU the library runs on
+ * holds from its first call until the process ends.  The call allocates,
+ * frees and memsets nothing (the workspace needs no clearing: the first
+ * backward kernel writes all of it that the others read).
+ *   - The device is the one current on the calling thread; `stream` must
+ *     belong to it.  The first call on a device looks up the array's address
+ *     there (hipGetSymbolAddress), later calls reuse it.
+ *   - Problems whose workspace (fa_bwd_workspace_bytes: two floats per query
+ *     row, B*H*N_q rows) exceeds the array get FA_ERR_UNSUPPORTED before
+ *     any HIP call.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on the same GPU (on other streams, from other threads) race and
+ *     give wrong gradients.  Calls ordered on one stream are safe.
+ * Other arguments and errors as for fa_bwd_ex. */
+#define FA_BWD_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)16 << 20)
+fa_status_t fa_bwd_noalloc(const fa_problem_t *p, const uint8_t *block_mask,
+                           int32_t mask_block, int64_t mask_head_stride,
+                           const void *q, const void *k, const void *v,
+                           const void *o, const float *lse, const void *dout,
+                           void *dq, void *dk, void *dv, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Other streaming reductions (math-properties page, section 8: softmax-based
  * routing and gating, LayerNorm and GroupNorm have attention's structure, a

@@ -306,6 +306,47 @@ def test_layernorm_rows_rejected(lib, args, status):
     assert lib.fa_last_error()
 
 
+def _noalloc(lib, p, mask=None, mb=128, **ptrs):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A)
+    a.update(ptrs)
+    return lib.fa_bwd_noalloc(ctypes.byref(p), mask, mb, 0, a["q"], a["k"], a["v"], a["o"], a["lse"],
+                              a["do"], a["dq"], a["dk"], a["dv"], None)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("bad_problem", INVALID), ("null_q", INVALID), ("misaligned_dk", UNSUPPORTED),
+    ("mask_block", INVALID), ("too_many_rows", UNSUPPORTED),
+])
+def test_noalloc_rejected_before_any_hip_call(lib, case, status):
+    """The allocation-free backward runs every check of fa_bwd, then refuses
+    a workspace beyond its static array -- all before any HIP call.  (A call
+    that passes the checks would launch, so none is made here.)"""
+    if case == "bad_problem":
+        assert _noalloc(lib, prob(head_dim=96)) == UNSUPPORTED
+        assert _noalloc(lib, prob(seqlen=0)) == status
+    elif case == "null_q":
+        assert _noalloc(lib, prob(), q=0) == status
+    elif case == "misaligned_dk":
+        assert _noalloc(lib, prob(), dk=A + 4) == status
+    elif case == "mask_block":
+        assert _noalloc(lib, prob(), mask=A, mb=100) == status
+    else:
+        # 32 heads x 65600 queries = 2,099,200 rows: 2 floats each exceed 16 MiB
+        N, H = 65600, 32
+        p = prob(batch=1, heads=H, seqlen=N, stride_b=H * N * 64, stride_h=N * 64, stride_n=64)
+        need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+        assert need > _lib.FA_BWD_NOALLOC_MAX_WORKSPACE_BYTES
+        assert _noalloc(lib, p) == status
+        assert "static" in lib.fa_last_error().decode()
+    assert lib.fa_last_error()
+
+
+def test_noalloc_limit_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define FA_BWD_NOALLOC_MAX_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.FA_BWD_NOALLOC_MAX_WORKSPACE_BYTES
+
+
 def _merge(lib, p, parts, lse_parts, o=A, lse=A, n=None):
     S = len(parts) if n is None else n
     op = None if parts is None else (ctypes.c_void_p * max(1, len(parts)))(*parts)
