@@ -295,12 +295,14 @@ def time_attention(args, w, dev, steps, warmup):
     common = dict(scale=w.scale, causal=w.causal, key_lens=kl)
     drop_seed = 0x5EED
 
+    qt = dict(query_tile=getattr(args, "query_tile", 0))
+
     def fwd(i):
         dr = dict(dropout_p=args.dropout, dropout_seed=drop_seed, dropout_offset=i)
         if bm is None:
-            fa_fwd(q, k, v, out=o, lse=lse, **common, **dr)
+            fa_fwd(q, k, v, out=o, lse=lse, **common, **dr, **qt)
         else:
-            fa_fwd_blocksparse(q, k, v, bm, mask_block=w.mb, out=o, lse=lse, **common, **dr)
+            fa_fwd_blocksparse(q, k, v, bm, mask_block=w.mb, out=o, lse=lse, **common, **dr, **qt)
 
     def bwd(stage, i):
         dr = dict(dropout_p=args.dropout, dropout_seed=drop_seed, dropout_offset=i)
@@ -426,6 +428,51 @@ def sweep_main(args, dev):
                       "sweep": rows}), flush=True)
 
 
+def tile_sweep_main(args, dev):
+    """The forward at B_r = 64, 128 and 256 queries per workgroup (2, 4 and 8
+    wavefronts) on the same inputs: bf16, d = 64, B = 1, H = 16, non-causal,
+    N = 8K, 16K and 32K.  Each (N, B_r) point is its own kernel instance
+    (template argument W = B_r / 32), so a rocprofv3 counter run of this mode
+    gives FETCH_SIZE per launch against B_r: the tile model's K / V re-read
+    term, 2 N^2 d e / B_r per head, scales as 1 / B_r unless the L2 holds the
+    K / V of a head (summary page, Complexity analysis: Theta(N^2 d^2 / M)).
+    Forward TFLOP/s from HIP events around each timed launch."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_33_amd import fa_fwd
+    from exact_io_aware_33_amd.inputs import make_inputs
+
+    calibration_copy(args, dev)
+    rows = []
+    stream = torch.cuda.current_stream(dev)
+    for N in (8192, 16384, 32768):
+        inp = make_inputs(1, 16, N, 64, "bf16", seed=0, with_do=False)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        flops = 4.0 * 16 * N * N * 64
+        for qt in (64, 128, 256):
+            def run():
+                fa_fwd(q, k, v, out=o, lse=lse, query_tile=qt)
+            warm_up(run, args.warmup)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for a, b in ev:
+                a.record(stream)
+                run()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            rows.append({"N": N, "B_r": qt, "grid_workgroups": 16 * ((N + qt - 1) // qt),
+                         "fwd_ms": round(ms, 4), "fwd_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                         "tile_model_kv_reread_bytes": 16 * 2 * N * 64 * 2 * ((N + qt - 1) // qt)})
+            log(f"[bench] tile sweep {rows[-1]}")
+        del q, k, v, o, lse
+    print(json.dumps({"mode": "tile_sweep", "B": 1, "H": 16, "d": 64, "dtype": "bf16", "causal": False,
+                      "steps": args.steps, "rows": rows}), flush=True)
+
+
 def reductions_main(args, dev):
     """The other streaming reductions: each case is timed with HIP events on
     the launch stream over `steps` launches; achieved = algorithmic bytes (read
@@ -542,6 +589,11 @@ def main():
     ap.add_argument("--scaling", action="store_true",
                     help="instead of the headline line, time fwd+bwd at B=1, H=16, d=64 bf16, "
                          "non-causal, N = 2K..32K (for HBM-byte scaling under rocprofv3 counters)")
+    ap.add_argument("--query-tile", type=int, default=0,
+                    help="queries per forward workgroup (0 = the library's choice; 64, 128, 256)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="instead of the headline line, time the forward at B_r = 64 / 128 / 256 "
+                         "(bf16, d=64, H=16, non-causal, N = 8K-32K; for FETCH_SIZE against B_r)")
     ap.add_argument("--reductions", action="store_true",
                     help="instead of the headline line, time the row softmax and LayerNorm / "
                          "GroupNorm kernels (HBM-bound) and print one JSON line")
@@ -566,6 +618,8 @@ def main():
         return sweep_main(args, dev)
     if args.reductions:
         return reductions_main(args, dev)
+    if args.tile_sweep:
+        return tile_sweep_main(args, dev)
     if args.scaling:
         return scaling_main(args, dev)
     if not w.backward:
@@ -613,7 +667,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_k": w.Nk, "d": w.d,
                    "causal": w.causal, "mask_block": w.mb, "key_padding": w.lens is not None,
-                   "dropout": args.dropout},
+                   "dropout": args.dropout, "fwd_query_tile": args.query_tile or "library"},
         "flop_count": ("4 B H N^2 d (halved when causal); backward 2.5x" if headline_count(w)
                        else "4 d per visible (query, key) pair; backward 2.5x"),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),

@@ -56,7 +56,8 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _problem(q, k, scale, causal, key_lens, dropout_p=0.0, dropout_seed=0, dropout_offset=0):
+def _problem(q, k, scale, causal, key_lens, dropout_p=0.0, dropout_seed=0, dropout_offset=0,
+             query_tile=0):
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
     if q.dtype not in _DTYPES:
@@ -81,7 +82,8 @@ def _problem(q, k, scale, causal, key_lens, dropout_p=0.0, dropout_seed=0, dropo
                   scale=float(scale), causal=1 if causal else 0, dtype=_DTYPES[q.dtype],
                   key_lens=None if key_lens is None else key_lens.data_ptr(),
                   dropout_p=float(dropout_p), dropout_offset=int(dropout_offset),
-                  dropout_seed=int(dropout_seed), seqlen_k=k.shape[2], reserved=0,
+                  dropout_seed=int(dropout_seed), seqlen_k=k.shape[2],
+                  fwd_query_tile=int(query_tile),
                   k_stride_b=k.stride(0), k_stride_h=k.stride(1), k_stride_n=k.stride(2))
     return p, key_lens
 
@@ -122,10 +124,12 @@ def _empty_like_layout(q):
 
 
 def fa_fwd(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=None,
-           dropout_p=0.0, dropout_seed=0, dropout_offset=0):
-    """Exact attention forward; returns (O, LSE).  Calls fa_fwd."""
+           dropout_p=0.0, dropout_seed=0, dropout_offset=0, query_tile=0):
+    """Exact attention forward; returns (O, LSE).  ``query_tile``: queries per
+    workgroup (0 = the library's choice, or 64 / 128 / 256).  Calls fa_fwd."""
     _same_layout(k, v)
-    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset,
+                     query_tile)
     o = _empty_like_layout(q) if out is None else out
     lse = _stats(lse, tuple(q.shape[:3]), q, "lse")
     _same_layout(q, o)
@@ -136,11 +140,12 @@ def fa_fwd(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=No
 
 def fa_fwd_blocksparse(q, k, v, block_mask, *, mask_block=128, scale=None, causal=False,
                        key_lens=None, out=None, lse=None, dropout_p=0.0, dropout_seed=0,
-                       dropout_offset=0):
+                       dropout_offset=0, query_tile=0):
     """Block-sparse forward; ``block_mask`` is uint8 [N/mb, N/mb] (shared by all heads)
     or [H, N/mb, N/mb].  Returns (O, LSE).  Calls fa_fwd_blocksparse."""
     _same_layout(k, v)
-    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset)
+    p, kl = _problem(q, k, scale, causal, key_lens, dropout_p, dropout_seed, dropout_offset,
+                     query_tile)
     bm, hstride = _mask(block_mask, q, k, mask_block)
     o = _empty_like_layout(q) if out is None else out
     lse = _stats(lse, tuple(q.shape[:3]), q, "lse")

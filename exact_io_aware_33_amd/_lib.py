@@ -39,7 +39,7 @@ class FaProblem(ctypes.Structure):
         ("dropout_offset", ctypes.c_uint32),
         ("dropout_seed", ctypes.c_uint64),
         ("seqlen_k", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("fwd_query_tile", ctypes.c_int32),
         ("k_stride_b", ctypes.c_int64),
         ("k_stride_h", ctypes.c_int64),
         ("k_stride_n", ctypes.c_int64),

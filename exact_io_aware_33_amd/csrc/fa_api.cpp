@@ -46,7 +46,9 @@ fa_status_t check_problem(const fa_problem_t *p) {
     return fail(FA_ERR_INVALID, "batch, heads and seqlen must be >= 1 (got %d, %d, %d)", p->batch,
                 p->heads, p->seqlen);
   if (p->seqlen_k < 0) return fail(FA_ERR_INVALID, "seqlen_k must be >= 0 (got %d)", p->seqlen_k);
-  if (p->reserved != 0) return fail(FA_ERR_INVALID, "reserved field must be 0");
+  if (p->fwd_query_tile != 0 && p->fwd_query_tile != 64 && p->fwd_query_tile != 128 &&
+      p->fwd_query_tile != 256)
+    return fail(FA_ERR_INVALID, "fwd_query_tile must be 0, 64, 128 or 256 (got %d)", p->fwd_query_tile);
   if (p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_F16 && p->dtype != FA_DTYPE_BF16)
     return fail(FA_ERR_INVALID, "unknown dtype %d", p->dtype);
   if (p->head_dim <= 0) return fail(FA_ERR_INVALID, "head_dim must be >= 1 (got %d)", p->head_dim);
@@ -140,6 +142,7 @@ fa::AttnParams make_params(const fa_problem_t *p) {
   a.drop_key0 = (uint32_t)(p->dropout_seed & 0xFFFFFFFFu);
   a.drop_key1 = (uint32_t)(p->dropout_seed >> 32);
   a.drop_offset = p->dropout_offset;
+  a.qtile = 128;
   return a;
 }
 
@@ -160,6 +163,11 @@ fa_status_t fwd_impl(const fa_problem_t *p, const uint8_t *mask, int32_t mb, int
     return st;
   if (sparse && (st = check_mask(p, mask, mb, hstride)) != FA_OK) return st;
   fa::AttnParams a = make_params(p);
+  a.qtile = p->fwd_query_tile ? p->fwd_query_tile : 128;
+  if (a.qtile != 128 && (p->dtype == FA_DTYPE_F32 || a.drop_thr != 0))
+    return fail(FA_ERR_UNSUPPORTED, "fwd_query_tile %d is built for fp16 / bf16 without dropout", a.qtile);
+  if (a.qtile == 256 && sparse)
+    return fail(FA_ERR_UNSUPPORTED, "fwd_query_tile 256 is not built for block masks");
   a.q = q;
   a.k = k;
   a.v = v;

@@ -44,7 +44,10 @@
 
 namespace fa {
 
-template <typename T, int D, bool SPARSE>
+// W: wavefronts per workgroup, so B_r = 32 W queries per workgroup (64, 128
+// or 256): the K / V tiles a workgroup streams through LDS serve that many
+// queries, so the K / V re-reads of the tile model scale as 1 / B_r.
+template <typename T, int D, bool SPARSE, int W = 4>
 struct FwdCfg {
   static constexpr int E = sizeof(T);
   static constexpr int KPL = Mma<T>::KPL;
@@ -54,10 +57,10 @@ struct FwdCfg {
   // (16K causal 0.69 vs 0.65 ms): LDS bandwidth is not what limits this
   // kernel.  The code keeps QB general.
   static constexpr int QB = 1;
-  static constexpr int WAVES = 4 / QB;
+  static constexpr int WAVES = W / QB;
   static constexpr int NTHR = 64 * WAVES;
   static constexpr int QPW = 32 * QB;             // queries per wavefront
-  static constexpr int BR = QPW * WAVES;          // queries per workgroup (128)
+  static constexpr int BR = QPW * WAVES;          // queries per workgroup (B_r)
   static constexpr int BC = (E == 4 || QB == 2) ? 32 : 64;  // keys per LDS tile
   static constexpr int NSB = BC / 32;             // 32-key score blocks per tile
   static constexpr int NBLK = QB * NSB;           // 32x32 score blocks per wave
@@ -78,7 +81,7 @@ struct FwdCfg {
   static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
   static constexpr int CPT = BC * CPR / NTHR;     // chunks per thread
   static_assert(BC * CPR % NTHR == 0, "tile must split evenly");
-  static_assert(BR == 128, "the block-sparse path needs 128-query workgroups");
+  static_assert(!SPARSE || 128 % BR == 0, "a block-sparse workgroup must lie in one mask block row");
 };
 
 constexpr int kMaxMaskBlocks = 1024;
@@ -100,13 +103,13 @@ constexpr float kMaxSlack = 8.0f;
 // SPLIT: the workgroup covers one of p.nsplit contiguous ranges of the key
 // tiles its query tile sees and writes an fp32 partial (O_s = sum p v / l_s,
 // LSE_s) for the merge kernel below.
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool SPLIT = false>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool SPLIT = false, int W = 4>
 // d = 64: registers bounded for three waves per SIMD (the few spills this
 // costs sit outside the tile loops); two with dropout, whose generator needs
 // the registers.
-__global__ void __launch_bounds__((FwdCfg<T, D, SPARSE>::NTHR), (D == 64 ? (DROP ? 2 : 3) : 1))
+__global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (DROP ? 2 : 3) : 1))
     fwd_kernel(AttnParams p) {
-  using C = FwdCfg<T, D, SPARSE>;
+  using C = FwdCfg<T, D, SPARSE, W>;
   using M = Mma<T>;
   using frag = typename M::frag;
   using LT = typename C::LT;
@@ -696,22 +699,38 @@ __global__ void __launch_bounds__(256) splitkv_merge_kernel(AttnParams p) {
   if (lane == 0) p.lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool SPLIT = false>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool SPLIT = false, int W = 4>
 static hipError_t launch_fwd_t(const AttnParams &p, hipStream_t s) {
-  using C = FwdCfg<T, D, SPARSE>;
+  using C = FwdCfg<T, D, SPARSE, W>;
   const int64_t nqt = (p.Nq + C::BR - 1) / C::BR;
   const int64_t grid = (int64_t)p.B * p.H * nqt * (SPLIT ? p.nsplit : 1);
   AttnParams a = p;
   void *args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE, DROP, SPLIT>),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE, DROP, SPLIT, W>),
                          dim3((unsigned)grid), dim3(C::NTHR), args, 0, s);
 }
 
+template <typename T, int D, bool DROP, int W>
+static hipError_t launch_fwd_w(const AttnParams &p, bool sparse, hipStream_t s) {
+  if (sparse) {
+    if constexpr (128 % (32 * W) == 0)
+      return p.causal ? launch_fwd_t<T, D, true, true, DROP, false, W>(p, s)
+                      : launch_fwd_t<T, D, false, true, DROP, false, W>(p, s);
+    return hipErrorInvalidValue;  // refused by the argument checks
+  }
+  return p.causal ? launch_fwd_t<T, D, true, false, DROP, false, W>(p, s)
+                  : launch_fwd_t<T, D, false, false, DROP, false, W>(p, s);
+}
+
+// Query tile: 128 unless the caller asked for 64 or 256 (16-bit types without
+// dropout only; the argument checks refuse the other combinations).
 template <typename T, int D, bool DROP>
 static hipError_t launch_fwd_dd(const AttnParams &p, bool sparse, hipStream_t s) {
-  if (sparse)
-    return p.causal ? launch_fwd_t<T, D, true, true, DROP>(p, s) : launch_fwd_t<T, D, false, true, DROP>(p, s);
-  return p.causal ? launch_fwd_t<T, D, true, false, DROP>(p, s) : launch_fwd_t<T, D, false, false, DROP>(p, s);
+  if constexpr (sizeof(T) == 2 && !DROP) {
+    if (p.qtile == 64) return launch_fwd_w<T, D, DROP, 2>(p, sparse, s);
+    if (p.qtile == 256) return launch_fwd_w<T, D, DROP, 8>(p, sparse, s);
+  }
+  return launch_fwd_w<T, D, DROP, 4>(p, sparse, s);
 }
 
 template <typename T, int D>

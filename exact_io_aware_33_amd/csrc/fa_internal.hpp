@@ -46,6 +46,8 @@ struct AttnParams {
   int32_t nsplit;
   float *part_o;             // [nsplit][B*H*N_q][d]
   float *part_lse;           // [nsplit][B*H*N_q]
+  // forward: queries per workgroup (64, 128 or 256); 128 for the other kernels
+  int32_t qtile;
 };
 
 // Merge of partial results over disjoint key sets (fa_merge.hip): part s is

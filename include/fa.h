@@ -107,9 +107,10 @@ typedef enum fa_status {
                               or negative scale, dropout_p outside [0, 1),
                               workspace too small, block size that does not
                               divide N_q and N_k, row stride below head_dim,
-                              nonzero reserved field                         */
+                              fwd_query_tile not 0, 64, 128 or 256           */
   FA_ERR_UNSUPPORTED = 2,  /* well-formed but not built: head_dim / dtype pair,
-                              block size not a multiple of 128, a pointer or
+                              block size not a multiple of 128, a query tile
+                              not built for the dtype / mask, a pointer or
                               stride that is not 16-byte aligned, sizes over
                               the 32-bit index / byte-offset ranges           */
   FA_ERR_HIP = 3           /* the HIP runtime refused a launch                 */
@@ -137,7 +138,14 @@ typedef struct fa_problem {
   uint32_t dropout_offset;  /* fourth Philox counter word (e.g. a step count) */
   uint64_t dropout_seed;    /* Philox key                                     */
   int32_t seqlen_k;         /* N_k: number of keys; 0 = N_q                    */
-  int32_t reserved;         /* must be 0                                      */
+  int32_t fwd_query_tile;   /* queries per forward workgroup, B_r: 0 = the
+                               library's choice (128), or 64, 128 or 256 (64
+                               and 256 for FP16 / BF16 without dropout; 256
+                               not with a block mask).  Read by fa_fwd and
+                               fa_fwd_blocksparse (the K / V tiles streamed
+                               through on-chip memory serve B_r queries, so
+                               re-reads of K and V scale as 1 / B_r); every
+                               other entry point requires 0 or ignores it    */
   int64_t k_stride_b;       /* K, V, dK, dV: element stride between batches;
                                all three k_stride_* 0 = the Q strides         */
   int64_t k_stride_h;       /*   ... between heads                            */

@@ -73,7 +73,8 @@ def test_status_strings(lib):
     ("seqlen", 1 << 30, UNSUPPORTED),
     ("dropout_p", -0.1, INVALID), ("dropout_p", 1.0, INVALID), ("dropout_p", 1.5, INVALID),
     ("dropout_p", float("nan"), INVALID), ("dropout_p", float("inf"), INVALID),
-    ("seqlen_k", -1, INVALID), ("seqlen_k", 1 << 30, UNSUPPORTED), ("reserved", 1, INVALID),
+    ("seqlen_k", -1, INVALID), ("seqlen_k", 1 << 30, UNSUPPORTED), ("fwd_query_tile", 1, INVALID),
+    ("fwd_query_tile", 96, INVALID), ("fwd_query_tile", -64, INVALID),
     ("k_stride_n", 60, INVALID), ("k_stride_h", -64, INVALID), ("k_stride_b", 4, INVALID),
 ])
 def test_problem_rejected_before_any_hip_call(lib, field, value, status):
@@ -380,3 +381,21 @@ def test_merge_rejected_before_any_hip_call(lib, case, status):
         st = _merge(lib, prob(head_dim=80), two, two)
     assert st == status
     assert lib.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,sparse", [
+    (dict(fwd_query_tile=64, dtype=_lib.FA_DTYPE_F32), False),
+    (dict(fwd_query_tile=256, dtype=_lib.FA_DTYPE_F32), False),
+    (dict(fwd_query_tile=64, dropout_p=0.1), False),
+    (dict(fwd_query_tile=256), True),
+])
+def test_query_tile_not_built_is_refused(lib, kw, sparse):
+    """Query tiles other than 128 exist for fp16 / bf16 without dropout; 256
+    not with a block mask (a workgroup must lie within one mask block row)."""
+    p = prob(**kw)
+    if sparse:
+        st = lib.fa_fwd_blocksparse(ctypes.byref(p), A, 128, 0, A, A, A, A, A, None)
+    else:
+        st = fwd(lib, p)
+    assert st == UNSUPPORTED
+    assert "fwd_query_tile" in lib.fa_last_error().decode()

@@ -58,16 +58,16 @@ def nan_like(t):
     return torch.full_like(t, float("nan"))
 
 
-def gpu_forward(inp, dtype, scale, causal, key_lens, mb, out_nan=True):
+def gpu_forward(inp, dtype, scale, causal, key_lens, mb, out_nan=True, query_tile=0):
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     kl = None if key_lens is None else key_lens.cuda()
     o = nan_like(q)
     lse = torch.full(q.shape[:3], float("nan"), device="cuda", dtype=torch.float32)
     if mb is None:
-        fa_fwd(q, k, v, scale=scale, causal=causal, key_lens=kl, out=o, lse=lse)
+        fa_fwd(q, k, v, scale=scale, causal=causal, key_lens=kl, out=o, lse=lse, query_tile=query_tile)
     else:
         fa_fwd_blocksparse(q, k, v, inp["block_mask"].cuda(), mask_block=mb, scale=scale,
-                           causal=causal, key_lens=kl, out=o, lse=lse)
+                           causal=causal, key_lens=kl, out=o, lse=lse, query_tile=query_tile)
     return (q, k, v, kl), o, lse
 
 
@@ -84,8 +84,9 @@ def gpu_backward(dev, inp, o, lse, scale, causal, mb):
 
 
 def check_case(B, H, N, d, dtype, *, causal=False, lens=None, key_lens=None, mb=None, density=0.3,
-               seed=0, backward=True, scale=None, block_mask=None, tol=None):
-    say(f"case B={B} H={H} N={N} d={d} {dtype} causal={causal} lens={lens} mb={mb} seed={seed}")
+               seed=0, backward=True, scale=None, block_mask=None, tol=None, query_tile=0):
+    say(f"case B={B} H={H} N={N} d={d} {dtype} causal={causal} lens={lens} mb={mb} seed={seed}"
+        f"{f' query_tile={query_tile}' if query_tile else ''}")
     inp = make_inputs(B, H, N, d, dtype, seed=seed, with_do=backward, lens=lens, mb=mb, density=density)
     if key_lens is not None:
         inp["key_lens"] = torch.tensor(key_lens, dtype=torch.int32)
@@ -93,7 +94,7 @@ def check_case(B, H, N, d, dtype, *, causal=False, lens=None, key_lens=None, mb=
         inp["block_mask"] = torch.as_tensor(block_mask, dtype=torch.uint8)
     scale = float(np.float32(1.0 / math.sqrt(d))) if scale is None else float(np.float32(scale))
     tol = TOL[dtype] if tol is None else tol
-    dev, o, lse = gpu_forward(inp, dtype, scale, causal, inp["key_lens"], mb)
+    dev, o, lse = gpu_forward(inp, dtype, scale, causal, inp["key_lens"], mb, query_tile=query_tile)
     if backward:
         dq, dk, dv = gpu_backward(dev, inp, o, lse, scale, causal, mb)
     torch.cuda.synchronize()
@@ -135,6 +136,41 @@ def test_forward_backward_small(dtype, d, mode, N):
     if "lens" in kw:
         kw["lens"] = (1, max(1, N))
     check_case(2, 3, N, d, dtype, seed=N + d, **kw)
+
+
+@pytest.mark.parametrize("query_tile", [64, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("N", [77, 300, 1000])
+def test_forward_query_tiles(query_tile, dtype, d, mode, N):
+    """The 64- and 256-query forward workgroups (2 and 8 wavefronts) against
+    the oracle: every mask mode, lengths that leave ragged last tiles."""
+    kw = dict(MODES[mode])
+    if "lens" in kw:
+        kw["lens"] = (1, N)
+    check_case(2, 3, N, d, dtype, seed=N + d + query_tile, backward=False, query_tile=query_tile, **kw)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_query_tile_64(dtype, causal):
+    check_case(2, 2, 1024, 64, dtype, causal=causal, mb=128, density=0.4, seed=17, backward=False,
+               query_tile=64)
+    check_case(1, 2, 512, 128, dtype, causal=causal, mb=256, density=0.5, seed=18, backward=False,
+               query_tile=64)
+
+
+def test_query_tiles_rank_major_and_bitwise_equal_rows():
+    """The query tile only regroups rows: each row's arithmetic is the same,
+    so O and LSE are bitwise equal across tiles 64 / 128 / 256 (16 heads, 8K
+    causal: rank-major order at 64 and 128, head by head at 256)."""
+    inp = make_inputs(1, 16, 8192, 64, "bf16", seed=5, with_do=False)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    outs = [fa_fwd(q, k, v, causal=True, query_tile=t) for t in (64, 128, 256)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
