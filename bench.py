@@ -54,15 +54,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The sources the attention kernels of a step (forward, backward, split-KV
+# forward and its merge) and their launches are built from; the row
+# reductions, the shard merge and the allocation-free entry point are not.
+STEP_SOURCES = ("fa_api.cpp", "fa_bwd.hip", "fa_device.hpp", "fa_dropout.hpp", "fa_fwd.hip",
+                "fa_internal.hpp")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the sources the attention kernels and their launches are
-    built from (all of csrc/ except the separate row-reduction kernels)."""
+    """sha256 over STEP_SOURCES and include/fa.h."""
     csrc = os.path.join(ROOT, "exact_io_aware_33_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")) and name != "fa_reduce.hip":
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in STEP_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     h.update(open(os.path.join(ROOT, "include", "fa.h"), "rb").read())
     return h.hexdigest()
 
@@ -120,9 +125,9 @@ def forward_flops(w, pairs) -> float:
 
 
 def dense_equivalent_flops(w) -> float:
-    """4 B H N_q N_k d (halved when causal): what the same shape would cost
-    with no mask, for context on masked workloads only."""
-    return 4.0 * w.B * w.H * w.N * w.Nk * w.d * (0.5 if w.causal else 1.0)
+    """4 B H N_q N_k d: what the same shape would cost with every (query,
+    key) pair visible, for context on masked workloads only."""
+    return 4.0 * w.B * w.H * w.N * w.Nk * w.d
 
 
 def traffic_from_profile(workload: str, kernel: str):
@@ -473,6 +478,92 @@ def tile_sweep_main(args, dev):
                       "steps": args.steps, "rows": rows}), flush=True)
 
 
+def ring_main(args, dev):
+    """One device's share of context-parallel (ring) attention at the per-hop
+    shape: bf16, d = 64, B = 1, H = 16, 16K local queries, 4 visiting K / V
+    shards of 16K keys (64K keys in all), non-causal.  Times (HIP events on
+    the stream) each hop's forward (fa_fwd, 16K x 16K), the merge of the 4
+    partial (O_s, LSE_s) (fa_merge_partials), each hop's backward with the
+    merged O and LSE (fa_bwd), and, for comparison, one fa_fwd over all 64K
+    keys.  The merge is HBM-bound: its algorithmic bytes are the S parts' O_s
+    and LSE_s read and O, LSE written."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_33_amd import fa_bwd, fa_fwd, fa_merge_partials
+    from exact_io_aware_33_amd.inputs import make_inputs
+
+    S, Ns, Nq, H, d = 4, 16384, 16384, 16, 64
+    inp = make_inputs(1, H, Nq, d, "bf16", seed=0, n_keys=S * Ns)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    # each visiting shard in a buffer of its own, as it arrives from a peer
+    ks = [k[:, :, s * Ns:(s + 1) * Ns].contiguous() for s in range(S)]
+    vs = [v[:, :, s * Ns:(s + 1) * Ns].contiguous() for s in range(S)]
+    o_parts = [torch.empty_like(q) for _ in range(S)]
+    l_parts = [torch.empty(q.shape[:3], dtype=torch.float32, device=dev) for _ in range(S)]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    grads = [(torch.empty_like(q), torch.empty_like(ks[0]), torch.empty_like(ks[0])) for _ in range(S)]
+    ws = torch.empty(16 * Nq * 8 + 1024, dtype=torch.uint8, device=dev)
+    o_all = torch.empty_like(q)
+    lse_all = torch.empty_like(lse)
+    stream = torch.cuda.current_stream(dev)
+
+    def hop_fwd(s):
+        fa_fwd(q, ks[s], vs[s], out=o_parts[s], lse=l_parts[s])
+
+    def merge():
+        fa_merge_partials(o_parts, l_parts, out=o, lse=lse)
+
+    def hop_bwd(s):
+        fa_bwd(q, ks[s], vs[s], o, lse, do, workspace=ws, dq=grads[s][0], dk=grads[s][1], dv=grads[s][2])
+
+    def whole():
+        fa_fwd(q, k, v, out=o_all, lse=lse_all)
+
+    def step():
+        for s in range(S):
+            hop_fwd(s)
+        merge()
+        for s in range(S):
+            hop_bwd(s)
+
+    warm_up(step, args.warmup)
+    warm_up(whole, args.warmup)
+    names = ["hop_fwd", "merge", "hop_bwd", "fwd_all_keys"]
+    times = {n: [] for n in names}
+    for _ in range(args.steps):
+        evs = []
+        for fn in ([lambda: hop_fwd(0)], [merge], [lambda: hop_bwd(0)], [whole]):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn[0]()
+            b.record(stream)
+            evs.append((a, b))
+        for s in range(1, S):  # keep every hop's partial fresh for the merge
+            hop_fwd(s)
+        torch.cuda.synchronize()
+        for n, (a, b) in zip(names, evs):
+            times[n].append(a.elapsed_time(b))
+    ms = {n: float(np.mean(t)) for n, t in times.items()}
+    hop_flops = 4.0 * H * Nq * Ns * d
+    rows = Nq * H
+    merge_bytes = S * rows * (d * 2 + 4) + rows * (d * 2 + 4)
+    out = {"mode": "ring", "shape": {"H": H, "d": d, "dtype": "bf16", "local_queries": Nq, "shards": S,
+                                     "keys_per_shard": Ns, "causal": False},
+           "steps": args.steps,
+           "hop_fwd_ms": round(ms["hop_fwd"], 4), "hop_fwd_tflops": round(hop_flops / (ms["hop_fwd"] * 1e-3) / 1e12, 1),
+           "hop_bwd_ms": round(ms["hop_bwd"], 4),
+           "hop_bwd_tflops": round(2.5 * hop_flops / (ms["hop_bwd"] * 1e-3) / 1e12, 1),
+           "merge_ms": round(ms["merge"], 4), "merge_bytes": merge_bytes,
+           "merge_GBs": round(merge_bytes / (ms["merge"] * 1e-3) / 1e9, 1),
+           "fwd_all_keys_ms": round(ms["fwd_all_keys"], 4),
+           "ring_fwd_vs_one_call": round((S * ms["hop_fwd"] + ms["merge"]) / ms["fwd_all_keys"], 4),
+           "xgmi_hop_bytes_per_head": 2 * Ns * d * 2}
+    log(f"[bench] ring {out}")
+    print(json.dumps(out), flush=True)
+
+
 def reductions_main(args, dev):
     """The other streaming reductions: each case is timed with HIP events on
     the launch stream over `steps` launches; achieved = algorithmic bytes (read
@@ -594,6 +685,10 @@ def main():
     ap.add_argument("--tile-sweep", action="store_true",
                     help="instead of the headline line, time the forward at B_r = 64 / 128 / 256 "
                          "(bf16, d=64, H=16, non-causal, N = 8K-32K; for FETCH_SIZE against B_r)")
+    ap.add_argument("--ring", action="store_true",
+                    help="instead of the headline line, time one device's hops of ring attention at the "
+                         "per-hop shape (16K queries x 4 shards of 16K keys, bf16, d=64, H=16) and the "
+                         "merge of their partial results")
     ap.add_argument("--reductions", action="store_true",
                     help="instead of the headline line, time the row softmax and LayerNorm / "
                          "GroupNorm kernels (HBM-bound) and print one JSON line")
@@ -620,6 +715,8 @@ def main():
         return reductions_main(args, dev)
     if args.tile_sweep:
         return tile_sweep_main(args, dev)
+    if args.ring:
+        return ring_main(args, dev)
     if args.scaling:
         return scaling_main(args, dev)
     if not w.backward:

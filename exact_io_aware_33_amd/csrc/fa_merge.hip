@@ -49,15 +49,27 @@ __global__ void __launch_bounds__(256) merge_parts_kernel(MergeParams p) {
   for (int e = 0; e < C::EPL; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (m != -INFINITY) {
-    for (int s = 0; s < p.S; ++s) {
-      const float w = expf(p.lse_parts[s][row] - m);
-      // a part that saw no key (LSE_s = -inf) weighs 0 whatever its O_s holds
-      if (w == 0.f) continue;
-      wsum += w;
-      const u32x4 raw = ldg16(static_cast<const char *>(p.o_parts[s]) + off);
-      const T *x = reinterpret_cast<const T *>(&raw);
+    // Parts in groups of kGroup: the group's loads are all in flight before
+    // the first is used.  A part that saw no key (LSE_s = -inf) weighs 0
+    // whatever its O_s holds (its terms are skipped by a select, not
+    // multiplied by 0, so a NaN there cannot leak in).
+    constexpr int kGroup = 4;
+    for (int s0 = 0; s0 < p.S; s0 += kGroup) {
+      u32x4 raw[kGroup];
+      float w[kGroup];
 #pragma unroll
-      for (int e = 0; e < C::EPL; ++e) acc[e] = fmaf(w, to_f32(x[e]), acc[e]);
+      for (int g = 0; g < kGroup; ++g) {
+        const int s = min(s0 + g, p.S - 1);
+        raw[g] = ldg16(static_cast<const char *>(p.o_parts[s]) + off);
+        w[g] = s0 + g < p.S ? expf(p.lse_parts[s][row] - m) : 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        wsum += w[g];
+        const T *x = reinterpret_cast<const T *>(&raw[g]);
+#pragma unroll
+        for (int e = 0; e < C::EPL; ++e) acc[e] = w[g] == 0.f ? acc[e] : fmaf(w[g], to_f32(x[e]), acc[e]);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
