@@ -454,10 +454,11 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   //
   // Generic iteration: any mask.  Straight-line code; past the last block the
   // next-block products are computed on a repeated block and never used.
-  auto iter_any = [&](int i, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
+  // `masked` false: block i is unmasked, the per-element mask is left out.
+  auto iter_any = [&](int i, auto masked, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
     fetch(i + C::AHEAD);
     const char *ql = slot(i), *qn = slot(i + 1);
-    softmax_grad(ql, qblock_start(i), SX, DX, ftrue{});
+    softmax_grad(ql, qblock_start(i), SX, DX, masked);
     sdp(qn, SY, DY);
     dvdk(ql, SX, DX);
     commit(i + C::AHEAD);
@@ -555,7 +556,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // the end of this key tile), or every block when the key tile crosses the
   // padding length.
   int n_masked = 0;
-  if (DROP || k0 + C::BKC > kv_len) {
+  if (k0 + C::BKC > kv_len) {
     n_masked = nq;
   } else if (CAUSAL) {
     while (n_masked < nq && qblock_start(n_masked) < k0 + C::BKC - cs) ++n_masked;
@@ -570,14 +571,14 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   };
   int i = 0;
   for (; i < n_masked && i < nq; ++i) {
-    iter_any(i, SA, DA, SB, DB);
+    iter_any(i, ftrue{}, SA, DA, SB, DB);
     swap_ab();
   }
   // Steady blocks in trips of NSLOT (so the slots are compile-time
   // constants); the trip must start at a block index that is 0 mod NSLOT.
   if constexpr (!DROP) {
     for (; i < nq - 1 && (i & (C::NSLOT - 1)) != 0; ++i) {
-      iter_any(i, SA, DA, SB, DB);
+      iter_any(i, ffalse{}, SA, DA, SB, DB);
       swap_ab();
     }
     using s0 = std::integral_constant<int, 0>;
@@ -591,8 +592,9 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
       iter_steady(i + 3, s3{}, SB, DB, SA, DA);
     }
   }
+  // the rest: unmasked blocks (with dropout: every block past the masked ones)
   for (; i < nq; ++i) {
-    iter_any(i, SA, DA, SB, DB);
+    iter_any(i, ffalse{}, SA, DA, SB, DB);
     swap_ab();
   }
 
@@ -635,6 +637,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   using frag = typename M::frag;
   constexpr int KPL = C::KPL, E = C::E;
   using LK = Layout<C::PITCH, C::ROWB, C::DMA>;
+  using ffalse = std::integral_constant<bool, false>;
   using ftrue = std::integral_constant<bool, true>;
 
   __shared__ __attribute__((aligned(1024))) char smem[C::NSLOT * C::SLOT];
@@ -857,7 +860,8 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   //
   // Generic iteration: any mask, straight-line; past the last tile the
   // next-tile products are computed on a repeated tile and never used.
-  auto iter_any = [&](int j, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
+  // `masked` false: tile j is unmasked, the per-element mask is left out.
+  auto iter_any = [&](int j, auto masked, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
     fetch(j + C::AHEAD);
     const char *kl = slot(j), *kn = slot(j + 1);
     const int lim_o = (CAUSAL ? min(kv_len, qi + 1 + cs) : kv_len) - tile_start(j);
@@ -867,7 +871,9 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
     for (int r = 0; r < 16; ++r) {
       if constexpr (DROP) grad_row_drop(SX, DX, r, keepb);
       else grad_row(SX, DX, r);
-      if (!(reg_row(r, 0) + 4 * h < lim_o)) DX[r] = 0.f;  // key kv0 + row invisible
+      if constexpr (decltype(masked)::value) {
+        if (!(reg_row(r, 0) + 4 * h < lim_o)) DX[r] = 0.f;  // key kv0 + row invisible
+      }
     }
     sdp(kn, SY, DY);
     dqacc(kl, DX);
@@ -954,8 +960,12 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
       iter_steady(j + 3, s3{}, SB, DB, SA, DA);
     }
   }
+  for (; j < min(n_full, ntiles); ++j) {  // unmasked
+    iter_any(j, ffalse{}, SA, DA, SB, DB);
+    swap_ab();
+  }
   for (; j < ntiles; ++j) {
-    iter_any(j, SA, DA, SB, DB);
+    iter_any(j, ftrue{}, SA, DA, SB, DB);
     swap_ab();
   }
 

@@ -444,8 +444,10 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
   //
   // Generic iteration: any mask, any visibility.  Straight-line code: a tile
   // that the wave cannot see is fully masked, so its exponentials are 0 and
-  // its PV adds nothing; past the last tile everything is masked.
-  auto iter_any = [&](int j, auto first, f32x16 (&X)[NBLK], f32x16 (&Y)[NBLK]) {
+  // its PV adds nothing; past the last tile everything is masked.  With
+  // `masked` false (tiles j and j+1 both unmasked: the dropout instances,
+  // which have no steady iteration) the per-element mask work is left out.
+  auto iter_any = [&](int j, auto first, auto masked, f32x16 (&X)[NBLK], f32x16 (&Y)[NBLK]) {
     fetch(true, stv, vslot(j), tile_start(j));
     fetch(false, stk, kslot(j), tile_start(min(j + 2, ntiles - 1)));
     if constexpr (!decltype(first)::value) pv(vslot(j - 1), Y, tile_start(j - 1));
@@ -455,12 +457,16 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
 #pragma unroll
       for (int e = qb * NSB * 16; e < (qb + 1) * NSB * 16; ++e) {
         const float x = fast_exp2(fmaf(EL(X, e), c2, -m_use));
-        EL(X, e) = EL(X, e) == -INFINITY ? 0.f : x;  // masked keys (also for scale 0)
+        if constexpr (decltype(masked)::value)
+          EL(X, e) = EL(X, e) == -INFINITY ? 0.f : x;  // masked keys (also for scale 0)
+        else
+          EL(X, e) = x;
       }
     }
     scores(kslot(j + 1), Y);
-    apply_mask(Y, j + 1 < ntiles ? tile_start(j + 1) : kv_len);  // all masked past the end
-    update_max(Y, X, ftrue{});
+    if constexpr (decltype(masked)::value)
+      apply_mask(Y, j + 1 < ntiles ? tile_start(j + 1) : kv_len);  // all masked past the end
+    update_max(Y, X, masked);
     commit(stv, vslot(j));
     commit(stk, kslot(j));
     __builtin_amdgcn_s_waitcnt(0);
@@ -574,10 +580,16 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
 
   int j = 0;
   if (ntiles > 0) {
-    iter_any(j++, ftrue{}, SB, SA);
+    iter_any(j++, ftrue{}, ftrue{}, SB, SA);
     rotate();
   }
-  if constexpr (!DROP) {
+  if constexpr (DROP) {
+    const int j_unmasked = min(n_full, ntiles) - 1;  // tiles j and j+1 unmasked
+    for (; j < j_unmasked; ++j) {
+      iter_any(j, ffalse{}, ffalse{}, SB, SA);
+      rotate();
+    }
+  } else {
     const int j_steady = min(n_full, ntiles) - 1;  // tiles j and j+1 unmasked
     // Two iterations per trip restore the roles at the loop back edge, so the
     // steady loop needs no register copies.
@@ -604,7 +616,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
     l32 = lane & 31;
   }
   for (; j < ntiles; ++j) {
-    iter_any(j, ffalse{}, SB, SA);
+    iter_any(j, ffalse{}, ftrue{}, SB, SA);
     rotate();
   }
   if (ntiles > 0) pv(vslot(ntiles - 1), SA, tile_start(ntiles - 1));
