@@ -12,8 +12,9 @@
 // With dropout (O = (P o Z) V, Z regenerated from the same Philox counters as
 // the forward's, fa_dropout.hpp) the same derivation with Z held fixed gives
 //     dV = (P o Z)^T dO,  dS = P * (Z o dP - D),  D_i = sum_c dO_ic O_ic
-// (D is unchanged in form: sum_j P_ij Z_ij dP_ij = dO_i . O_i); those
-// instances (DROP) take the generic iteration for every block.
+// (D is unchanged in form: sum_j P_ij Z_ij dP_ij = dO_i . O_i).  In those
+// instances (DROP) the steady iterations generate the next block's keep
+// bytes while the current block is processed.
 //
 // Kernels (all on the caller's stream):
 //  1. bwd_pre:   D = rowsum(dO * O) per query row (the only workspace: one
@@ -475,27 +476,49 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // LDS-DMA is spread over the first groups.  `par` is i mod NSLOT (a
   // compile-time constant in the unrolled loop, so every LDS address is a
   // loop-invariant register plus an immediate).
-  auto iter_steady = [&](int i, auto par, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
+  // With DROP, KX holds the keep bytes of block i (its dP MFMAs started from
+  // 0, -D enters per row as in softmax_grad) and the generator rounds for
+  // block i+1's bytes (into KY) ride one per MFMA group.
+  static_assert(!DROP || NGA + NGB >= kPhiloxRounds, "one generator round per MFMA group");
+  auto iter_steady = [&](int i, auto par, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY,
+                         uint32_t (&KX)[4], uint32_t (&KY)[4]) {
     constexpr int P = decltype(par)::value;
     char *const ql = smem + P * C::SLOT;
     char *const qn = smem + ((P + 1) % C::NSLOT) * C::SLOT;
     const float *ll = reinterpret_cast<const float *>(ql + C::LSE_OFF);
-    f32x4 l4[2];
+    const float *dd = reinterpret_cast<const float *>(ql + C::D_OFF);
+    f32x4 l4[2], nd4[2];
     // P, dS of row r (quad q = r / 4 prefetched one quad ahead)
     auto row = [&](int r) {
       const int q = r >> 2, j = r & 3;
-      if (j == 0 && q + 1 < 4)
+      if (j == 0 && q + 1 < 4) {
         l4[(q + 1) & 1] = *reinterpret_cast<const f32x4 *>(ll + 8 * (q + 1) + 4 * h);
+        if constexpr (DROP) nd4[(q + 1) & 1] = *reinterpret_cast<const f32x4 *>(dd + 8 * (q + 1) + 4 * h);
+      }
       const float pv = fast_exp2(fmaf(SX[r], c2, -l4[q & 1][j]));
-      SX[r] = pv;
-      DX[r] = pv * DX[r];
+      if constexpr (DROP) {
+        const bool kp = kept(KX, r, p.drop_thr);
+        SX[r] = kp ? pv : 0.f;
+        DX[r] = pv * fmaf(kp ? p.drop_scale : 0.f, DX[r], nd4[q & 1][j]);
+      } else {
+        SX[r] = pv;
+        DX[r] = pv * DX[r];
+      }
     };
+    auto gen = [&](int grp) {
+      if constexpr (DROP) {
+        if (grp < kPhiloxRounds) philox_round(KY, p.drop_key0, p.drop_key1, grp);
+        if (grp == kPhiloxRounds - 1) keep_finish_key_col(KY, lane);
+      }
+    };
+    if constexpr (DROP) keep_ctr_key_col(KY, p, bh, qblock_start(i + 1), key, lane);
     // ---- score / dP MFMAs of block i+1
     frag af[3];
     af[0] = qfrag(qn, sdp_order(0));
     af[1] = qfrag(qn, sdp_order(1));
-    const f32x16 negd_n = load_negd(qn);
+    const f32x16 negd_n = DROP ? f32x16{} : load_negd(qn);
     l4[0] = *reinterpret_cast<const f32x4 *>(ll + 4 * h);
+    if constexpr (DROP) nd4[0] = *reinterpret_cast<const f32x4 *>(dd + 4 * h);
     SY = f32x16{};
     FA_FENCE();
 #pragma unroll
@@ -507,6 +530,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
       if (g <= C::CPTQ) fetch1(i + C::AHEAD, g);
 #pragma unroll
       for (int r = 8 * g / NGA; r < 8 * (g + 1) / NGA; ++r) row(r);
+      gen(g);
       FA_FENCE();
     }
     // ---- dV / dK MFMAs of block i
@@ -531,6 +555,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
         pb[(t + 1) & 1] = pack_frag<T>(SX, (t + 1) * KPL);
         sbf[(t + 1) & 1] = pack_frag<T>(DX, (t + 1) * KPL);
       }
+      gen(NGA + g);
       FA_FENCE();
     }
     commit(i + C::AHEAD);
@@ -576,7 +601,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   }
   // Steady blocks in trips of NSLOT (so the slots are compile-time
   // constants); the trip must start at a block index that is 0 mod NSLOT.
-  if constexpr (!DROP) {
+  {
     for (; i < nq - 1 && (i & (C::NSLOT - 1)) != 0; ++i) {
       iter_any(i, ffalse{}, SA, DA, SB, DB);
       swap_ab();
@@ -585,11 +610,13 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     using s1 = std::integral_constant<int, 1>;
     using s2 = std::integral_constant<int, 2>;
     using s3 = std::integral_constant<int, 3>;
+    uint32_t KA[4], KB[4];  // keep bytes of the current / next block (DROP)
+    if (DROP && i + C::NSLOT < nq) keep_bytes_key_col(KA, p, bh, qblock_start(i), key, lane);
     for (; i + C::NSLOT < nq; i += C::NSLOT) {
-      iter_steady(i, s0{}, SA, DA, SB, DB);
-      iter_steady(i + 1, s1{}, SB, DB, SA, DA);
-      iter_steady(i + 2, s2{}, SA, DA, SB, DB);
-      iter_steady(i + 3, s3{}, SB, DB, SA, DA);
+      iter_steady(i, s0{}, SA, DA, SB, DB, KA, KB);
+      iter_steady(i + 1, s1{}, SB, DB, SA, DA, KB, KA);
+      iter_steady(i + 2, s2{}, SA, DA, SB, DB, KA, KB);
+      iter_steady(i + 3, s3{}, SB, DB, SA, DA, KB, KA);
     }
   }
   // the rest: unmasked blocks (with dropout: every block past the masked ones)
@@ -885,10 +912,26 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   // packing of step 0), the first half of the NGB dQ MFMAs carry the last 8
   // rows; operand reads two groups ahead; the next tile's LDS-DMA spread over
   // the first groups.  `par` is j mod NSLOT (compile-time slot addresses).
-  auto iter_steady = [&](int j, auto par, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY) {
+  // With DROP, KX holds the keep bytes of tile j and the generator rounds for
+  // tile j+1's (into KY) ride one per MFMA group.
+  constexpr int NGRP = NGA + NGB;
+  static_assert(!DROP || NGRP >= kPhiloxRounds, "one generator round per MFMA group");
+  auto iter_steady = [&](int j, auto par, f32x16 &SX, f32x16 &DX, f32x16 &SY, f32x16 &DY,
+                         uint32_t (&KX)[4], uint32_t (&KY)[4]) {
     constexpr int P = decltype(par)::value;
     char *const kl = smem + P * C::SLOT;
     char *const kn = smem + ((P + 1) % C::NSLOT) * C::SLOT;
+    auto row = [&](int r) {
+      if constexpr (DROP) grad_row_drop(SX, DX, r, KX);
+      else grad_row(SX, DX, r);
+    };
+    auto gen = [&](int grp) {
+      if constexpr (DROP) {
+        if (grp < kPhiloxRounds) philox_round(KY, p.drop_key0, p.drop_key1, grp);
+        if (grp == kPhiloxRounds - 1) keep_finish_query_col(KY, lane);
+      }
+    };
+    if constexpr (DROP) keep_ctr_query_col(KY, p, bh, qi, tile_start(j + 1), lane);
     frag af[3];
     af[0] = kvfrag(kn, 0);
     af[1] = kvfrag(kn, 1);
@@ -898,11 +941,12 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
     for (int g = 0; g < NGA; ++g) {
       const int s = g >> 1;
       if (g + 2 < NGA) af[(g + 2) % 3] = kvfrag(kn, g + 2);
-      if (g & 1) DY = M::mma32(af[g % 3], gf[s], s == 0 ? negd : DY);
+      if (g & 1) DY = M::mma32(af[g % 3], gf[s], s == 0 ? (DROP ? f32x16{} : negd) : DY);
       else SY = M::mma32(af[g % 3], qf[s], SY);
       if (g < C::CPT) fetch1(j + C::AHEAD, g);
 #pragma unroll
-      for (int r = 8 * g / NGA; r < 8 * (g + 1) / NGA; ++r) grad_row(SX, DX, r);
+      for (int r = 8 * g / NGA; r < 8 * (g + 1) / NGA; ++r) row(r);
+      gen(g);
       FA_FENCE();
     }
     frag tf[3], sf[2];
@@ -917,9 +961,10 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
       qacc[nb] = M::mma32(tf[g % 3], sf[t & 1], qacc[nb]);
       if (g < NGB / 2) {
 #pragma unroll
-        for (int r = 8 + 8 * g / (NGB / 2); r < 8 + 8 * (g + 1) / (NGB / 2); ++r) grad_row(SX, DX, r);
+        for (int r = 8 + 8 * g / (NGB / 2); r < 8 + 8 * (g + 1) / (NGB / 2); ++r) row(r);
       }
       if (g % C::NOB == C::NOB - 1 && t + 1 < C::PSTEPS) sf[(t + 1) & 1] = pack_frag<T>(DX, (t + 1) * KPL);
+      gen(NGA + g);
       FA_FENCE();
     }
     commit(j + C::AHEAD);
@@ -951,13 +996,15 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   using s1 = std::integral_constant<int, 1>;
   using s2 = std::integral_constant<int, 2>;
   using s3 = std::integral_constant<int, 3>;
-  if constexpr (!DROP) {
+  {
     const int j_steady = min(n_full, ntiles - 1);  // tile j unmasked, j+1 exists
+    uint32_t KA[4], KB[4];  // keep bytes of the current / next tile (DROP)
+    if (DROP && j + C::NSLOT <= j_steady) keep_bytes_query_col(KA, p, bh, qi, tile_start(j), lane);
     for (; j + C::NSLOT <= j_steady; j += C::NSLOT) {
-      iter_steady(j, s0{}, SA, DA, SB, DB);
-      iter_steady(j + 1, s1{}, SB, DB, SA, DA);
-      iter_steady(j + 2, s2{}, SA, DA, SB, DB);
-      iter_steady(j + 3, s3{}, SB, DB, SA, DA);
+      iter_steady(j, s0{}, SA, DA, SB, DB, KA, KB);
+      iter_steady(j + 1, s1{}, SB, DB, SA, DA, KB, KA);
+      iter_steady(j + 2, s2{}, SA, DA, SB, DB, KA, KB);
+      iter_steady(j + 3, s3{}, SB, DB, SA, DA, KB, KA);
     }
   }
   for (; j < min(n_full, ntiles); ++j) {  // unmasked

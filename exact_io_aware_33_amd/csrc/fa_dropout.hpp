@@ -28,22 +28,35 @@
 
 namespace fa {
 
+// Round r (or rounds R0 .. R1-1) of Philox4x32-10 on the counter c, (k0, k1)
+// being the key of round 0 (round r uses it bumped r times by the Weyl
+// constants).  Split so that a kernel can spread one generator call over
+// several groups of matrix instructions.
+// (r is a constant wherever the caller's loop is unrolled, and so are the
+// round keys' increments.)
+__device__ __forceinline__ void philox_round(uint32_t (&c)[4], uint32_t k0, uint32_t k1, int r) {
+  k0 += (uint32_t)r * 0x9E3779B9u;
+  k1 += (uint32_t)r * 0xBB67AE85u;
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+  const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+  const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+  c[1] = (uint32_t)p1;
+  c[3] = (uint32_t)p0;
+  c[0] = n0;
+  c[2] = n2;
+}
+template <int R0, int R1>
+__device__ __forceinline__ void philox_rounds(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = R0; r < R1; ++r) philox_round(c, k0, k1, r);
+}
+constexpr int kPhiloxRounds = 10;
+
 // Philox4x32-10 on the counter c under key (k0, k1); c is replaced by the
 // four output words.
 __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
-    c[1] = (uint32_t)p1;
-    c[3] = (uint32_t)p0;
-    c[0] = n0;
-    c[2] = n2;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
+  philox_rounds<0, kPhiloxRounds>(c, k0, k1);
 }
 
 // Value of x held by quad lane (own ^ X), X = 1, 2, 3 (DPP quad_perm).
@@ -92,30 +105,45 @@ __device__ __forceinline__ void byte_transpose(uint32_t (&x)[4]) {
 // Decision bytes of a 32x32 tile whose column (lane) is query qi and whose
 // rows are the keys kb + reg_row(r, h) (forward, dQ kernels; kb a multiple of
 // 32, qi = lane mod 4): on return byte k of x[g] decides register 4g + k.
-__device__ __forceinline__ void keep_bytes_query_col(uint32_t (&x)[4], const AttnParams &p, int bh,
-                                                     int qi, int kb, int lane) {
+// In stages: the counter (keep_ctr_query_col), the ten rounds
+// (philox_rounds), the exchange across the quad (keep_finish_query_col).
+__device__ __forceinline__ void keep_ctr_query_col(uint32_t (&x)[4], const AttnParams &p, int bh, int qi,
+                                                   int kb, int lane) {
   const int w = lane & 3, h = (lane >> 5) & 1;
   x[0] = (uint32_t)qi >> 2;
   x[1] = (uint32_t)((kb >> 2) + 2 * w + h);  // quad lane w: keys kb + 8w + 4h + 0..3
   x[2] = (uint32_t)bh;
   x[3] = p.drop_offset;
+}
+__device__ __forceinline__ void keep_finish_query_col(uint32_t (&x)[4], int lane) { quad_transpose(x, lane); }
+__device__ __forceinline__ void keep_bytes_query_col(uint32_t (&x)[4], const AttnParams &p, int bh,
+                                                     int qi, int kb, int lane) {
+  keep_ctr_query_col(x, p, bh, qi, kb, lane);
   philox4x32_10(x, p.drop_key0, p.drop_key1);
-  quad_transpose(x, lane);
+  keep_finish_query_col(x, lane);
 }
 
 // Decision bytes of a 32x32 tile whose column (lane) is key `key` and whose
 // rows are the queries q0 + reg_row(r, h) (dK/dV kernel; q0 a multiple of 32,
 // key = lane mod 4): on return byte k of x[g] decides register 4g + k.
-__device__ __forceinline__ void keep_bytes_key_col(uint32_t (&x)[4], const AttnParams &p, int bh,
-                                                   int q0, int key, int lane) {
+// Stages as for keep_bytes_query_col.
+__device__ __forceinline__ void keep_ctr_key_col(uint32_t (&x)[4], const AttnParams &p, int bh, int q0,
+                                                 int key, int lane) {
   const int w = lane & 3, h = (lane >> 5) & 1;
   x[0] = (uint32_t)((q0 >> 2) + 2 * w + h);  // quad lane w: queries q0 + 8w + 4h + 0..3
   x[1] = (uint32_t)key >> 2;
   x[2] = (uint32_t)bh;
   x[3] = p.drop_offset;
-  philox4x32_10(x, p.drop_key0, p.drop_key1);
+}
+__device__ __forceinline__ void keep_finish_key_col(uint32_t (&x)[4], int lane) {
   byte_transpose(x);  // x[k] byte u: query 4 G + u, key 4 (key / 4) + k
   quad_transpose(x, lane);
+}
+__device__ __forceinline__ void keep_bytes_key_col(uint32_t (&x)[4], const AttnParams &p, int bh,
+                                                   int q0, int key, int lane) {
+  keep_ctr_key_col(x, p, bh, q0, key, lane);
+  philox4x32_10(x, p.drop_key0, p.drop_key1);
+  keep_finish_key_col(x, lane);
 }
 
 // Whether register r of the tile is kept.

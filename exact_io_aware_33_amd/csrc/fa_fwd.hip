@@ -98,8 +98,7 @@ constexpr float kMaxSlack = 8.0f;
 // the issue order.
 #define FA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// DROP: dropout on P (keep decisions regenerated per tile, see fa_dropout.hpp);
-// every tile then takes the generic iteration.
+// DROP: dropout on P (keep decisions regenerated per tile, see fa_dropout.hpp).
 // SPLIT: the workgroup covers one of p.nsplit contiguous ranges of the key
 // tiles its query tile sees and writes an fp32 partial (O_s = sum p v / l_s,
 // LSE_s) for the merge kernel below.
@@ -444,10 +443,8 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
   //
   // Generic iteration: any mask, any visibility.  Straight-line code: a tile
   // that the wave cannot see is fully masked, so its exponentials are 0 and
-  // its PV adds nothing; past the last tile everything is masked.  With
-  // `masked` false (tiles j and j+1 both unmasked: the dropout instances,
-  // which have no steady iteration) the per-element mask work is left out.
-  auto iter_any = [&](int j, auto first, auto masked, f32x16 (&X)[NBLK], f32x16 (&Y)[NBLK]) {
+  // its PV adds nothing; past the last tile everything is masked.
+  auto iter_any = [&](int j, auto first, f32x16 (&X)[NBLK], f32x16 (&Y)[NBLK]) {
     fetch(true, stv, vslot(j), tile_start(j));
     fetch(false, stk, kslot(j), tile_start(min(j + 2, ntiles - 1)));
     if constexpr (!decltype(first)::value) pv(vslot(j - 1), Y, tile_start(j - 1));
@@ -457,16 +454,12 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
 #pragma unroll
       for (int e = qb * NSB * 16; e < (qb + 1) * NSB * 16; ++e) {
         const float x = fast_exp2(fmaf(EL(X, e), c2, -m_use));
-        if constexpr (decltype(masked)::value)
-          EL(X, e) = EL(X, e) == -INFINITY ? 0.f : x;  // masked keys (also for scale 0)
-        else
-          EL(X, e) = x;
+        EL(X, e) = EL(X, e) == -INFINITY ? 0.f : x;  // masked keys (also for scale 0)
       }
     }
     scores(kslot(j + 1), Y);
-    if constexpr (decltype(masked)::value)
-      apply_mask(Y, j + 1 < ntiles ? tile_start(j + 1) : kv_len);  // all masked past the end
-    update_max(Y, X, masked);
+    apply_mask(Y, j + 1 < ntiles ? tile_start(j + 1) : kv_len);  // all masked past the end
+    update_max(Y, X, ftrue{});
     commit(stv, vslot(j));
     commit(stk, kslot(j));
     __builtin_amdgcn_s_waitcnt(0);
@@ -481,13 +474,43 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
   // Operand reads run two groups ahead of their MFMA.  `par` is the parity of
   // j (a compile-time constant in the unrolled loop, so every LDS address is
   // a loop-invariant register plus an immediate).
-  auto iter_steady = [&](int j, auto par, f32x16 (&X)[NBLK], f32x16 (&Y)[NBLK]) {
+  //
+  // With dropout (QB = 1): KX holds the keep bytes of tile j-1, applied to the
+  // PV operands as they are packed (after their row sums: l sums P, not
+  // P o Z); the generator rounds for tile j's bytes (into KY, one call per
+  // 32-key block) ride on the MFMA groups of both phases.
+  constexpr int NGRP = NG1 + NG2;                 // MFMA groups per iteration
+  static_assert(!DROP || (QB == 1 && NGRP % NSB == 0), "dropout steady iteration: one query block per wave");
+  auto iter_steady = [&](int j, auto par, f32x16 (&X)[NBLK], f32x16 (&Y)[NBLK], uint32_t (&KX)[NSB][4],
+                         uint32_t (&KY)[NSB][4]) {
     constexpr int P = decltype(par)::value;
     const char *vl = vslot(P ^ 1), *kl = kslot(P ^ 1);
     const int kv_v = tile_start(j), kv_k = tile_start(min(j + 2, ntiles - 1));
     float m_use[QB];  // finite: every lane sees a key of tile j
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m_use[qb] = m_run[qb];
+    // generator rounds of MFMA group G: block G / GB, rounds spread evenly
+    constexpr int GB = NGRP / NSB;
+    auto gen = [&](int G) {
+      if constexpr (DROP) {
+        const int sb = G / GB, g = G - sb * GB;
+#pragma unroll
+        for (int r = g * kPhiloxRounds / GB; r < (g + 1) * kPhiloxRounds / GB; ++r)
+          philox_round(KY[sb], p.drop_key0, p.drop_key1, r);
+        if (g == GB - 1) keep_finish_query_col(KY[sb], lane);
+      }
+    };
+    if constexpr (DROP) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) keep_ctr_query_col(KY[sb], p, bh, qw0 + l32, kv_v + 32 * sb, lane);
+    }
+    // with DROP: row sum of the packed operand, then the keep mask
+    auto drop_op = [&](frag &f, int sb, int t) {
+      if constexpr (DROP) {
+        rowsum(0, f);
+        f = drop_frag<T>(f, KX[sb], t * KPL, p.drop_thr, drop_add);
+      }
+    };
     // ---- A
     frag vf[3], pbf[2][QB];
     auto vf_of = [&](int g) { return vfrag(vl, g / C::NOB, g % C::NOB); };
@@ -495,6 +518,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
     if (NG1 > 1) vf[1] = vf_of(1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) pbf[0][qb] = pack_frag<T>(Y[qb * NSB], 0);
+    drop_op(pbf[0][0], 0, 0);
     FA_FENCE();
 #pragma unroll
     for (int g = 0; g < NG1; ++g) {
@@ -513,13 +537,17 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
           const int sb = (k + 1) / C::PSTEPS, t = (k + 1) - sb * C::PSTEPS;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) pbf[cb ^ 1][qb] = pack_frag<T>(Y[qb * NSB + sb], t * KPL);
+          drop_op(pbf[cb ^ 1][0], sb, t);
         }
+        if constexpr (!DROP) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) rowsum(qb, pbf[cb][qb]);
+          for (int qb = 0; qb < QB; ++qb) rowsum(qb, pbf[cb][qb]);
+        }
       }
 #pragma unroll
       for (int e = g * NEL / NG1; e < (g + 1) * NEL / NG1; ++e)
         EL(X, e) = fmaf(EL(X, e), c2, -m_use[e / (NSB * 16)]);
+      gen(g);
       FA_FENCE();
     }
     // ---- B
@@ -536,6 +564,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
         Y[qb * NSB + sb] = M::mma32(kf[i % 3], qf[qb][s], s == 0 ? f32x16{} : Y[qb * NSB + sb]);
 #pragma unroll
       for (int e = i * NEL / NG2; e < (i + 1) * NEL / NG2; ++e) EL(X, e) = fast_exp2(EL(X, e));
+      gen(NG1 + i);
       FA_FENCE();
     }
     // ---- C
@@ -580,27 +609,27 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
 
   int j = 0;
   if (ntiles > 0) {
-    iter_any(j++, ftrue{}, ftrue{}, SB, SA);
+    iter_any(j++, ftrue{}, SB, SA);
     rotate();
   }
-  if constexpr (DROP) {
-    const int j_unmasked = min(n_full, ntiles) - 1;  // tiles j and j+1 unmasked
-    for (; j < j_unmasked; ++j) {
-      iter_any(j, ffalse{}, ffalse{}, SB, SA);
-      rotate();
-    }
-  } else {
+  {
     const int j_steady = min(n_full, ntiles) - 1;  // tiles j and j+1 unmasked
     // Two iterations per trip restore the roles at the loop back edge, so the
     // steady loop needs no register copies.
     using odd = std::integral_constant<int, 1>;
     using even = std::integral_constant<int, 0>;
+    uint32_t KA[NSB][4], KB[NSB][4];  // keep bytes of the previous / current tile (DROP)
+    if (DROP && j < j_steady) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+        keep_bytes_query_col(KA[sb], p, bh, qw0 + l32, tile_start(j - 1) + 32 * sb, lane);
+    }
     for (; j + 1 < j_steady; j += 2) {
-      iter_steady(j, odd{}, SB, SA);
-      iter_steady(j + 1, even{}, SA, SB);
+      iter_steady(j, odd{}, SB, SA, KA, KB);
+      iter_steady(j + 1, even{}, SA, SB, KB, KA);
     }
     if (j < j_steady) {
-      iter_steady(j++, odd{}, SB, SA);
+      iter_steady(j++, odd{}, SB, SA, KA, KB);
       rotate();
     }
   }
@@ -616,7 +645,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
     l32 = lane & 31;
   }
   for (; j < ntiles; ++j) {
-    iter_any(j, ffalse{}, ftrue{}, SB, SA);
+    iter_any(j, ffalse{}, SB, SA);
     rotate();
   }
   if (ntiles > 0) pv(vslot(ntiles - 1), SA, tile_start(ntiles - 1));

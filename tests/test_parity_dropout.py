@@ -130,17 +130,23 @@ def test_dropout_rates(p):
 
 
 # ------------------------------------------------------ exact keep decisions
-def _mask_inputs(B, H, N, which):
-    """Q = 0 (uniform P); V, dO and K the identity in the role that reads
-    the mask out of the chosen kernel."""
-    z = torch.zeros(B, H, N, N, dtype=torch.float32)
-    eye = torch.eye(N, dtype=torch.float32).expand(B, H, N, N).contiguous()
-    ones = torch.ones(B, H, N, N, dtype=torch.float32)
+def _mask_inputs(B, H, N, which, blk=0):
+    """Q = 0 (uniform P); V, dO and K chosen so that one kernel's output reads
+    out the keep mask of the key (or query) columns blk*d .. blk*d + d - 1,
+    d = min(N, 128): E[j, c] = 1 iff j = blk*d + c selects those columns and
+    R[j, c] = 1 iff j = c (mod d) has one 1 in every row."""
+    d = min(N, 128)
+    z = torch.zeros(B, H, N, d, dtype=torch.float32)
+    ones = torch.ones(B, H, N, d, dtype=torch.float32)
+    rows = torch.arange(N)[:, None]
+    cols = torch.arange(d)[None, :]
+    sel = (rows == blk * d + cols).float().expand(B, H, N, d).contiguous()
+    rep = (rows % d == cols).float().expand(B, H, N, d).contiguous()
     if which == "fwd":
-        return dict(q=z, k=ones, v=eye, do=ones)
+        return dict(q=z, k=ones, v=sel, do=ones)
     if which == "dv":
-        return dict(q=z, k=ones, v=ones, do=eye)
-    return dict(q=z, k=eye, v=eye, do=ones)   # dQ: dP = 1, so dS = P (Z - D)
+        return dict(q=z, k=ones, v=ones, do=sel)
+    return dict(q=z, k=sel, v=rep, do=ones)   # dQ: dP = 1, so dS = P (Z - D)
 
 
 def _oracle_mask(B, H, N, drop):
@@ -150,27 +156,34 @@ def _oracle_mask(B, H, N, drop):
                      for b in range(B)])
 
 
+# N = 512 takes every kernel through its steady (software-pipelined) loop,
+# where the keep bytes of the next tile are generated a tile ahead; the
+# columns are then read out 128 at a time.
+@pytest.mark.parametrize("shape", [(2, 3, 128), (1, 2, 512)])
 @pytest.mark.parametrize("drop", [(0.5, 2024, 0), (0.25, (7 << 32) | 11, 123456)])
-def test_keep_decisions_bit_exact_in_all_three_kernels(drop):
-    B, H, N = 2, 3, 128
+def test_keep_decisions_bit_exact_in_all_three_kernels(drop, shape):
+    B, H, N = shape
     ref = _oracle_mask(B, H, N, drop)
     t = oracle.drop_threshold(drop[0])
     zscale = np.float32(256.0 / (256.0 - t))
-    say(f"case mask readout B={B} H={H} N={N} dropout={drop}")
-    # forward: O_i[j] = Z_ij / N
-    o, _, _ = run(_mask_inputs(B, H, N, "fwd"), 1.0, drop=drop, backward=False)
-    o = o.cpu().numpy()
-    assert np.array_equal(o != 0, ref)
-    assert np.all(o[ref] == np.float32(zscale / N))
-    # dK/dV kernel: dV_j[i] = Z_ij / N
-    _, _, (_, _, dv) = run(_mask_inputs(B, H, N, "dv"), 1.0, drop=drop)
-    dv = dv.cpu().numpy()
-    assert np.array_equal(np.swapaxes(dv, 2, 3) != 0, ref)
-    # dQ kernel: dQ_i[j] = (Z_ij - D_i) / N, two values per row, the larger kept
-    _, _, (dq, _, _) = run(_mask_inputs(B, H, N, "dq"), 1.0, drop=drop)
-    dq = dq.cpu().numpy().astype(np.float64)
-    mid = 0.5 * (dq.max(axis=3, keepdims=True) + dq.min(axis=3, keepdims=True))
-    assert np.array_equal(dq > mid, ref)
+    d = min(N, 128)
+    for blk in range(N // d):
+        cs = slice(blk * d, (blk + 1) * d)
+        say(f"case mask readout B={B} H={H} N={N} dropout={drop} columns {blk * d}..{(blk + 1) * d - 1}")
+        # forward: O_i[c] = Z_i,(blk d + c) / N
+        o, _, _ = run(_mask_inputs(B, H, N, "fwd", blk), 1.0, drop=drop, backward=False)
+        o = o.cpu().numpy()
+        assert np.array_equal(o != 0, ref[..., cs])
+        assert np.all(o[ref[..., cs]] == np.float32(zscale / N))
+        # dK/dV kernel: dV_j[c] = Z_(blk d + c),j / N
+        _, _, (_, _, dv) = run(_mask_inputs(B, H, N, "dv", blk), 1.0, drop=drop)
+        dv = dv.cpu().numpy()
+        assert np.array_equal(np.swapaxes(dv, 2, 3) != 0, ref[:, :, cs, :])
+        # dQ kernel: dQ_i[c] = (Z_i,(blk d + c) - D_i) / N, two values per row, the larger kept
+        _, _, (dq, _, _) = run(_mask_inputs(B, H, N, "dq", blk), 1.0, drop=drop)
+        dq = dq.cpu().numpy().astype(np.float64)
+        mid = 0.5 * (dq.max(axis=3, keepdims=True) + dq.min(axis=3, keepdims=True))
+        assert np.array_equal(dq > mid, ref[..., cs])
     say(f"  kept fraction {ref.mean():.4f} (expected {1 - t / 256:.4f})")
 
 
