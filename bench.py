@@ -209,6 +209,42 @@ def calibration_copy(args, dev):
     del src, dst
 
 
+def gemm_reference(dtype, dev, n=8192, iters=10):
+    """TFLOP/s of a plain n^3 matrix product in `dtype` through torch.matmul
+    (the vendor GEMM library) on standard-normal operands, timed right after
+    the attention step (clock already settled).  The matrix cores' rate
+    depends on the data as well as on the instruction stream (the chip is
+    power-limited under dense MFMA work; the same product on zeros runs about
+    1.35x faster), so this is the practical ceiling for dense 16-bit MFMA work
+    on data like the benchmark's -- context for the roofline, not its peak."""
+    import torch
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(dtype)
+    if dt is None:
+        return None
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(n, n, device=dev, dtype=dt, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=dt, generator=g)
+
+    def rate(x, y):
+        for _ in range(3):
+            c = x @ y
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            c = x @ y
+        e1.record()
+        torch.cuda.synchronize()
+        del c
+        return 2.0 * n ** 3 / (e0.elapsed_time(e1) / iters * 1e-3) / 1e12
+
+    t_rand = rate(a, b)
+    a.zero_()
+    t_zero = rate(a, a)
+    del a, b
+    return {"op": f"torch.matmul {dtype} {n}x{n}x{n}, standard-normal operands",
+            "tflops": round(t_rand, 1), "tflops_zero_operands": round(t_zero, 1)}
+
+
 def decode_main(args, w, dev):
     """One split-KV forward per step on a forward-only (decoding) workload."""
     import numpy as np
@@ -667,6 +703,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the plain-GEMM rate reported beside the roofline")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="fused dropout probability (0 = none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -787,6 +825,12 @@ def main():
                      "traffic": traffic, "flops_per_launch": alg_flops,
                      "avg_launch_ms": round(dur_ms, 4)},
     }
+    if not args.no_gemm_reference:
+        ref = gemm_reference(w.dtype, dev)
+        if ref is not None:
+            ref["roofline_achieved_frac_of_gemm"] = round(achieved / ref["tflops"], 4)
+            out["gemm_reference"] = ref
+            log(f"[bench] gemm reference {ref}")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (cpu_baseline)...")
         out["cpu_baseline"] = cpu_baseline(
