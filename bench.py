@@ -209,7 +209,7 @@ def calibration_copy(args, dev):
     del src, dst
 
 
-def gemm_reference(dtype, dev, n=8192, iters=10):
+def gemm_reference(dtype, dev, n=8192, iters=20):
     """TFLOP/s of a plain n^3 matrix product in `dtype` through torch.matmul
     (the vendor GEMM library) on standard-normal operands, timed right after
     the attention step (clock already settled).  The matrix cores' rate
@@ -226,8 +226,12 @@ def gemm_reference(dtype, dev, n=8192, iters=10):
     b = torch.randn(n, n, device=dev, dtype=dt, generator=g)
 
     def rate(x, y):
-        for _ in range(3):
+        c = x @ y
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:  # the clock settles on the new load
             c = x @ y
+            torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(iters):
