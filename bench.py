@@ -314,7 +314,9 @@ def time_attention(args, w, dev, steps, warmup):
     """Time `steps` whole steps of workload `w` after `warmup` untimed ones.
 
     Returns the inputs, the wall-clock ms per step and the HIP-event averages
-    (ms) of the forward and of the three backward launches."""
+    (ms) of the forward, of the dQ pass (with the preprocessing of its rows:
+    one call with FA_BWD_PRE | FA_BWD_DQ) and of the dK/dV pass -- the launch
+    sequence of fa_bwd, split in two calls so each is timed."""
     import numpy as np
     import torch
 
@@ -360,15 +362,12 @@ def time_attention(args, w, dev, steps, warmup):
         fwd(i)
         if ev is not None:
             ev[1].record(stream)
-        bwd(FA_BWD_PRE, i)
+        bwd(FA_BWD_PRE | FA_BWD_DQ, i)
         if ev is not None:
             ev[2].record(stream)
         bwd(FA_BWD_MAIN, i)
         if ev is not None:
             ev[3].record(stream)
-        bwd(FA_BWD_DQ, i)
-        if ev is not None:
-            ev[4].record(stream)
 
     # The W warm-up steps asked for, then more until at least MIN_WARMUP_S of
     # warm-up has run: the shader clock takes ~0.1-0.2 s of load to settle,
@@ -389,7 +388,7 @@ def time_attention(args, w, dev, steps, warmup):
     time_attention.extra_warmup = extra
     log(f"[bench] warmup {warmup} steps (+{extra} to reach {MIN_WARMUP_S} s) done")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -398,11 +397,10 @@ def time_attention(args, w, dev, steps, warmup):
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    pre_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    dq_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     main_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-    dq_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
     log(f"[bench] timed {steps} steps: {ms_step:.3f} ms/step; fwd {fwd_ms:.3f} ms, "
-        f"bwd pre {pre_ms:.3f} / main {main_ms:.3f} / dq {dq_ms:.3f} ms")
+        f"bwd dq (with the preprocessing) {dq_ms:.3f} / main {main_ms:.3f} ms")
 
     if getattr(args, "graph", False):
         # The same step recorded once into a HIP graph and replayed: what the
@@ -431,7 +429,7 @@ def time_attention(args, w, dev, steps, warmup):
         time_attention.eager_alt_ms = float(np.median(eager))
         log(f"[bench] interleaved: eager {time_attention.eager_alt_ms:.3f} / graph "
             f"{time_attention.graph_ms:.3f} ms/step")
-    return inputs, ms_step, fwd_ms, pre_ms, main_ms, dq_ms
+    return inputs, ms_step, fwd_ms, main_ms, dq_ms
 
 
 def sweep_main(args, dev):
@@ -451,12 +449,12 @@ def sweep_main(args, dev):
             # at least ~10 steps' worth of the 16K problem per point, so the
             # short problems are not timed over a few milliseconds only
             reps = max(1, 16384 // N)
-            _, ms_step, fwd_ms, pre_ms, main_ms, dq_ms = time_attention(
+            _, ms_step, fwd_ms, main_ms, dq_ms = time_attention(
                 args, w, dev, args.steps * reps, args.warmup * reps)
             f_fwd = forward_flops(w, None)
             rows.append({"N": N, "B": w.B, "H": w.H, "causal": causal,
                          "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 1),
-                         "bwd_tflops": round(2.5 * f_fwd / ((pre_ms + main_ms + dq_ms) * 1e-3) / 1e12, 1),
+                         "bwd_tflops": round(2.5 * f_fwd / ((main_ms + dq_ms) * 1e-3) / 1e12, 1),
                          "fwd_bwd_tflops": round(3.5 * f_fwd / (ms_step * 1e-3) / 1e12, 1),
                          "ms_per_step": round(ms_step, 4),
                          **({"graph_fwd_bwd_tflops": round(
@@ -464,8 +462,8 @@ def sweep_main(args, dev):
                              "eager_fwd_bwd_tflops_interleaved": round(
                              3.5 * f_fwd / (time_attention.eager_alt_ms * 1e-3) / 1e12, 1)}
                             if args.graph else {}),
-                         "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
-                                       "bwd_main": round(main_ms, 4), "bwd_dq": round(dq_ms, 4)}})
+                         "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_main": round(main_ms, 4),
+                                       "bwd_dq": round(dq_ms, 4)}})
             log(f"[bench] sweep {rows[-1]}")
     print(json.dumps({"metric": "attention TFLOP/s fwd & fwd+bwd, N=1K-16K d=64 bf16; % of MFMA peak",
                       "unit": "TFLOP/s", "peak": MFMA_PEAK_TFLOPS["bf16"], "steps": args.steps,
@@ -688,12 +686,12 @@ def scaling_main(args, dev):
     rows = []
     for N in (2048, 4096, 8192, 16384, 32768):
         w = Workload(f"scaling_n{N}", 1, 16, N, 64, "bf16")
-        _, ms_step, fwd_ms, pre_ms, main_ms, dq_ms = time_attention(args, w, dev, args.steps,
+        _, ms_step, fwd_ms, main_ms, dq_ms = time_attention(args, w, dev, args.steps,
                                                                     args.warmup)
         f_fwd = forward_flops(w, None)
         rows.append({"N": N, "fwd_bwd_tflops": round(3.5 * f_fwd / (ms_step * 1e-3) / 1e12, 1),
-                     "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
-                                   "bwd_main": round(main_ms, 4), "bwd_dq": round(dq_ms, 4)},
+                     "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_main": round(main_ms, 4),
+                                   "bwd_dq": round(dq_ms, 4)},
                      "grid_workgroups": 16 * (N // 128)})
         log(f"[bench] scaling {rows[-1]}")
     print(json.dumps({"mode": "scaling", "B": 1, "H": 16, "d": 64, "dtype": "bf16", "causal": False,
@@ -763,7 +761,7 @@ def main():
         return scaling_main(args, dev)
     if not w.backward:
         return decode_main(args, w, dev)
-    inputs, ms_step, fwd_ms, pre_ms, main_ms, dq_ms = time_attention(
+    inputs, ms_step, fwd_ms, main_ms, dq_ms = time_attention(
         args, w, dev, args.steps, args.warmup)
 
     pairs = visible_pairs(w, None if inputs["key_lens"] is None else inputs["key_lens"].numpy(),
@@ -810,9 +808,9 @@ def main():
         "flop_count": ("4 B H N^2 d (halved when causal); backward 2.5x" if headline_count(w)
                        else "4 d per visible (query, key) pair; backward 2.5x"),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
-        "bwd_tflops": round(2.5 * f_fwd / ((pre_ms + main_ms + dq_ms) * 1e-3) / 1e12, 3),
+        "bwd_tflops": round(2.5 * f_fwd / ((main_ms + dq_ms) * 1e-3) / 1e12, 3),
         "mfma_peak_frac_step": round(alg_step / (ms_step * 1e-3) / 1e12 / peak, 4),
-        "bwd_algorithmic_frac": round(10.0 * w.d * pairs / ((pre_ms + main_ms + dq_ms) * 1e-3)
+        "bwd_algorithmic_frac": round(10.0 * w.d * pairs / ((main_ms + dq_ms) * 1e-3)
                                       / 1e12 / peak, 4),
         "kernel_tflops": kernel_tflops,
         **({} if headline_count(w) else {"dense_equivalent_tflops": round(
@@ -822,8 +820,8 @@ def main():
             "graph_tflops": round(f_step / (time_attention.graph_ms * 1e-3) / 1e12, 3),
             "eager_ms_per_step_interleaved": round(time_attention.eager_alt_ms, 4)}
            if args.graph else {}),
-        "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_pre": round(pre_ms, 4),
-                      "bwd_main": round(main_ms, 4), "bwd_dq": round(dq_ms, 4)},
+        "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_main": round(main_ms, 4),
+                      "bwd_dq": round(dq_ms, 4)},
         "roofline": {"kernel": name, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "flops_per_launch": alg_flops,

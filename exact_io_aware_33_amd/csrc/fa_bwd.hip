@@ -760,13 +760,57 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
       qf[s] = *reinterpret_cast<const frag *>(qrow + s * KPL);
       gf[s] = *reinterpret_cast<const frag *>(grow + s * KPL);
     }
-    lse2 = p.ws_lse2[(int64_t)bh * Nq + qi];  // +inf when no key is visible: P = 0
-    negdl = p.ws_negd[(int64_t)bh * Nq + qi];
+    if (!p.dq_pre) {
+      lse2 = p.ws_lse2[(int64_t)bh * Nq + qi];  // +inf when no key is visible: P = 0
+      negdl = p.ws_negd[(int64_t)bh * Nq + qi];
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
       qf[s] = frag{};
       gf[s] = frag{};
+    }
+  }
+  if (p.dq_pre) {
+    // The preprocessing step for this lane's query, bitwise as bwd_pre_kernel
+    // computes it: the row's 16-byte chunks of O and dO (LPR of them) each
+    // give an FMA chain, and the chunk sums meet pairwise at strides LPR/2,
+    // LPR/4, ..., 1 (the preprocessing kernel's xor shuffles).  This lane
+    // holds the chunks of its half row (its dO ones are already in gf); the
+    // stride-LPR/2 pairs are this lane's and its partner's (lane ^ 32).
+    constexpr int EPC = 16 / E, LPR = D * E / 16, HALF = LPR / 2;
+    const T *O = static_cast<const T *>(p.o_in) + base;
+    float cs_[HALF];
+#pragma unroll
+    for (int c = 0; c < HALF; ++c) {
+      u32x4 ov = u32x4{};
+      if (qi < Nq) ov = ldg16(reinterpret_cast<const char *>(O + (int64_t)qi * p.sn + h * (D / 2)) + 16 * c);
+      const T *ot = reinterpret_cast<const T *>(&ov);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const int idx = c * EPC + e;  // element of the half row
+        T g;
+        if constexpr (KPL == 1) g = gf[idx];
+        else g = gf[idx / KPL][idx % KPL];
+        acc = fmaf((float)ot[e], (float)g, acc);
+      }
+      cs_[c] = acc;
+    }
+#pragma unroll
+    for (int c = 0; c < HALF; ++c) cs_[c] = cs_[c] + xor32(cs_[c]);
+#pragma unroll
+    for (int w = HALF / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int c = 0; c < w; ++c) cs_[c] = cs_[c] + cs_[c + w];
+    if (qi < Nq) {
+      negdl = -cs_[0];
+      const float l = p.lse[(int64_t)bh * Nq + qi];
+      lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+      if (h == 0) {  // for the dK/dV pass, which runs after this one
+        p.ws_negd[(int64_t)bh * Nq + qi] = negdl;
+        p.ws_lse2[(int64_t)bh * Nq + qi] = lse2;
+      }
     }
   }
   f32x16 negd;
@@ -1068,6 +1112,25 @@ static hipError_t launch_bwd_dd(const AttnParams &p, bool sparse, unsigned stage
   void *args[] = {&a};
   const int64_t rows = (int64_t)p.B * p.H * p.Nq;
   hipError_t e = hipSuccess;
+  auto main_pass = [&]() {
+    if (sparse)
+      return p.causal ? launch_main_t<T, D, true, true, DROP>(p, s) : launch_main_t<T, D, false, true, DROP>(p, s);
+    return p.causal ? launch_main_t<T, D, true, false, DROP>(p, s) : launch_main_t<T, D, false, false, DROP>(p, s);
+  };
+  auto dq_pass = [&](const AttnParams &q) {
+    if (sparse)
+      return q.causal ? launch_dq_t<T, D, true, true, DROP>(q, s) : launch_dq_t<T, D, false, true, DROP>(q, s);
+    return q.causal ? launch_dq_t<T, D, true, false, DROP>(q, s) : launch_dq_t<T, D, false, false, DROP>(q, s);
+  };
+  if ((stages & FA_BWD_PRE) && (stages & FA_BWD_DQ)) {
+    // The dQ pass does the preprocessing of its own queries and fills the
+    // workspace; the dK/dV pass, if asked for, runs after it.
+    AttnParams f = p;
+    f.dq_pre = 1;
+    if ((e = dq_pass(f)) != hipSuccess) return e;
+    if (stages & FA_BWD_MAIN) e = main_pass();
+    return e;
+  }
   if (stages & FA_BWD_PRE) {
     constexpr int rpb = PreCfg<T, D>::RPB;
     e = hipLaunchKernel(reinterpret_cast<const void *>(&bwd_pre_kernel<T, D>),
@@ -1075,18 +1138,9 @@ static hipError_t launch_bwd_dd(const AttnParams &p, bool sparse, unsigned stage
     if (e != hipSuccess) return e;
   }
   if (stages & FA_BWD_MAIN) {
-    if (sparse)
-      e = p.causal ? launch_main_t<T, D, true, true, DROP>(p, s) : launch_main_t<T, D, false, true, DROP>(p, s);
-    else
-      e = p.causal ? launch_main_t<T, D, true, false, DROP>(p, s) : launch_main_t<T, D, false, false, DROP>(p, s);
-    if (e != hipSuccess) return e;
+    if ((e = main_pass()) != hipSuccess) return e;
   }
-  if (stages & FA_BWD_DQ) {
-    if (sparse)
-      e = p.causal ? launch_dq_t<T, D, true, true, DROP>(p, s) : launch_dq_t<T, D, false, true, DROP>(p, s);
-    else
-      e = p.causal ? launch_dq_t<T, D, true, false, DROP>(p, s) : launch_dq_t<T, D, false, false, DROP>(p, s);
-  }
+  if (stages & FA_BWD_DQ) e = dq_pass(p);
   return e;
 }
 

@@ -48,6 +48,10 @@ struct AttnParams {
   float *part_lse;           // [nsplit][B*H*N_q]
   // forward: queries per workgroup (64, 128 or 256); 128 for the other kernels
   int32_t qtile;
+  // backward: the dQ pass computes -D and LSE*log2(e) of its own queries (in
+  // the preprocessing kernel's arithmetic) and writes them to the workspace,
+  // instead of reading what the preprocessing kernel wrote
+  int32_t dq_pre;
 };
 
 // Merge of partial results over disjoint key sets (fa_merge.hip): part s is

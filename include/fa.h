@@ -278,7 +278,8 @@ typedef enum fa_bwd_stage {
   FA_BWD_MAIN = 2,   /* key-stationary pass: recompute S, P per tile; write
                         dK, dV (reads the workspace)                         */
   FA_BWD_DQ = 4,     /* query-stationary pass: recompute S, P per tile; write
-                        dQ (reads the workspace; independent of FA_BWD_MAIN) */
+                        dQ (reads the workspace, or fills it when PRE is in
+                        the same call; independent of FA_BWD_MAIN)           */
   FA_BWD_ALL = 7
 } fa_bwd_stage_t;
 
@@ -286,9 +287,14 @@ typedef enum fa_bwd_stage {
  * a caller can time a stage on its own or put other work between stages.
  * block_mask == NULL selects the dense path (mask_block, mask_head_stride
  * ignored); otherwise the arguments mean what they mean for
- * fa_bwd_blocksparse.  `stages` is a nonzero subset of FA_BWD_ALL; the
- * stages it names run in the order PRE, MAIN, DQ.  Calling with PRE, then
- * MAIN, then DQ on one stream, with the same workspace, gives exactly the
+ * fa_bwd_blocksparse.  `stages` is a nonzero subset of FA_BWD_ALL.  When it
+ * holds both PRE and DQ, the dQ pass does the preprocessing of its own
+ * queries (bitwise the values the PRE stage writes) and fills the workspace,
+ * with no separate preprocessing launch, and MAIN, if named, runs after it;
+ * otherwise the named stages run in the order PRE, MAIN, DQ.  So FA_BWD_ALL
+ * launches two kernels (dQ, then dK/dV), and PRE | DQ followed by MAIN is
+ * the same sequence in two calls.  Calling with PRE, then MAIN, then DQ (or
+ * DQ before MAIN) on one stream, with the same workspace, gives exactly the
  * result of one call with FA_BWD_ALL; MAIN and DQ may also run concurrently
  * (on two streams) once PRE has completed.  Arguments a stage does not read
  * are still checked. */

@@ -280,24 +280,36 @@ def test_forward_is_bitwise_reproducible():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_backward_is_bitwise_reproducible_and_stage_split_matches():
-    """No atomics: the backward is deterministic, and running its three stages
-    through fa_bwd_ex (here MAIN and DQ in the opposite order, which the ABI
-    allows once PRE is done) gives exactly fa_bwd's result."""
-    inp = make_inputs(2, 3, 700, 64, "bf16", seed=4)
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f16", 128), ("f32", 64), ("f32", 128)])
+def test_backward_is_bitwise_reproducible_and_stage_split_matches(dtype, d):
+    """No atomics: the backward is deterministic, and running its stages
+    through fa_bwd_ex gives exactly fa_bwd's result: PRE, then DQ, then MAIN
+    (MAIN and DQ in either order once PRE is done), and PRE | DQ (the dQ pass
+    doing the preprocessing itself, as fa_bwd does) then MAIN.  The workspace
+    the fused dQ pass leaves is bitwise the preprocessing kernel's."""
+    inp = make_inputs(2, 3, 700, d, dtype, seed=4)
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
     o, lse = fa_fwd(q, k, v, causal=True)
     g1 = fa_bwd(q, k, v, o, lse, do, causal=True)
     g2 = fa_bwd(q, k, v, o, lse, do, causal=True)
-    ws = torch.full((fa_bwd_workspace_bytes(q, causal=True),), 255, dtype=torch.uint8, device="cuda")
-    g3 = tuple(torch.full_like(q, float("nan")) for _ in range(3))
-    common = dict(causal=True, workspace=ws, dq=g3[0], dk=g3[1], dv=g3[2])
-    fa_bwd_ex(q, k, v, o, lse, do, FA_BWD_PRE, **common)
-    fa_bwd_ex(q, k, v, o, lse, do, FA_BWD_DQ, **common)
-    fa_bwd_ex(q, k, v, o, lse, do, FA_BWD_MAIN, **common)
+    nws = fa_bwd_workspace_bytes(q, causal=True)
+    results, spaces = [], []
+    for order in ([FA_BWD_PRE, FA_BWD_DQ, FA_BWD_MAIN], [FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ],
+                  [FA_BWD_PRE | FA_BWD_DQ, FA_BWD_MAIN]):
+        ws = torch.full((nws,), 255, dtype=torch.uint8, device="cuda")
+        g3 = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+        common = dict(causal=True, workspace=ws, dq=g3[0], dk=g3[1], dv=g3[2])
+        for st in order:
+            fa_bwd_ex(q, k, v, o, lse, do, st, **common)
+        results.append(g3)
+        spaces.append(ws)
     torch.cuda.synchronize()
-    for a, b, c in zip(g1, g2, g3):
-        assert torch.equal(a, b) and torch.equal(a, c)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    for g3 in results:
+        for a, c in zip(g1, g3):
+            assert torch.equal(a, c)
+    assert torch.equal(spaces[0], spaces[2])
 
 
 def test_binding_and_library_reject_bad_calls_on_gpu():
