@@ -33,7 +33,10 @@
 //                dQ^T += K^T dS^T with K^T read through the transposing LDS
 //                read.  dQ is written once per row: no atomics, and the result
 //                does not depend on scheduling.
-// bwd_main and bwd_dq both read D and are independent of each other.
+// bwd_main and bwd_dq both read D and are independent of each other.  The
+// full sequence (fa_bwd) is two launches: bwd_dq with dq_pre set does step 1
+// for its own queries (bitwise as bwd_pre does it) and fills the workspace,
+// then bwd_main; bwd_pre runs when a caller asks for that stage alone.
 #include <type_traits>
 
 #include "fa_device.hpp"
