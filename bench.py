@@ -396,9 +396,12 @@ def time_attention(args, w, dev, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    dq_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    main_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    per = {"fwd": [e[0].elapsed_time(e[1]) for e in events],
+           "bwd_dq": [e[1].elapsed_time(e[2]) for e in events],
+           "bwd_main": [e[2].elapsed_time(e[3]) for e in events]}
+    fwd_ms, dq_ms, main_ms = (float(np.mean(per[n])) for n in ("fwd", "bwd_dq", "bwd_main"))
+    time_attention.spread = {"kernel_ms_median": {n: round(float(np.median(v)), 4) for n, v in per.items()},
+                             "kernel_ms_min": {n: round(float(np.min(v)), 4) for n, v in per.items()}}
     log(f"[bench] timed {steps} steps: {ms_step:.3f} ms/step; fwd {fwd_ms:.3f} ms, "
         f"bwd dq (with the preprocessing) {dq_ms:.3f} / main {main_ms:.3f} ms")
 
@@ -822,6 +825,7 @@ def main():
            if args.graph else {}),
         "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_main": round(main_ms, 4),
                       "bwd_dq": round(dq_ms, 4)},
+        **time_attention.spread,
         "roofline": {"kernel": name, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "flops_per_launch": alg_flops,
