@@ -678,6 +678,74 @@ def reductions_main(args, dev):
                       "warmup": args.warmup, "data": "synthetic", "cases": rows_out}), flush=True)
 
 
+def standard_contrast_main(args, dev):
+    """Standard attention next to this library's step on the same inputs:
+    B=1, H=16, d=64, bf16, non-causal, N = 2K, 4K, 8K (or the one N of
+    --contrast-n).  Standard attention here is the textbook sequence with
+    every N x N matrix in HBM -- S = scale Q K^T and P = softmax(S) (fp32
+    softmax, P stored in bf16), O = P V; backward dV = P^T dO, dP = dO V^T,
+    dS = P (dP - D), dQ = dS K, dK = dS^T Q -- as plain torch batched
+    products on contiguous operands.  Both run a fixed number of steps
+    (warm-up + timed, printed), so a counter run of one N divides its HBM
+    bytes by that count: the contrast the pages draw between standard and
+    IO-aware attention, measured."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_33_amd import fa_bwd, fa_fwd
+
+    ns = (args.contrast_n,) if args.contrast_n else (2048, 4096, 8192)
+    B, H, d = 1, 16, 64
+    scale = 1.0 / math.sqrt(d)
+    calibration_copy(args, dev)
+    rows = []
+    for N in ns:
+        g = torch.Generator().manual_seed(N)
+        q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(dev) for _ in range(4))
+        q3, k3, v3, do3 = (t.reshape(B * H, N, d).contiguous() for t in (q, k, v, do))
+
+        def standard():
+            s = torch.bmm(q3, k3.transpose(1, 2).contiguous()) * scale
+            p = torch.softmax(s.float(), dim=-1).to(torch.bfloat16)
+            o = torch.bmm(p, v3)
+            dv = torch.bmm(p.transpose(1, 2).contiguous(), do3)
+            dp = torch.bmm(do3, v3.transpose(1, 2).contiguous())
+            dd = (do3.float() * o.float()).sum(-1, keepdim=True)
+            ds = (p.float() * (dp.float() - dd) * scale).to(torch.bfloat16)
+            dq = torch.bmm(ds, k3)
+            dk = torch.bmm(ds.transpose(1, 2).contiguous(), q3)
+            return o, dq, dk, dv
+
+        def ours():
+            o, lse = fa_fwd(q, k, v, scale=scale)
+            return fa_bwd(q, k, v, o, lse, do, scale=scale)
+
+        res = {"N": N}
+        for name, fn in (("standard", standard), ("library", ours)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            res[f"{name}_ms"] = round(float(np.mean([a.elapsed_time(b) for a, b in ev])), 4)
+        f = 3.5 * 4.0 * B * H * N * N * d
+        res["standard_tflops"] = round(f / (res["standard_ms"] * 1e-3) / 1e12, 1)
+        res["library_tflops"] = round(f / (res["library_ms"] * 1e-3) / 1e12, 1)
+        res["nxn_bytes_per_matrix"] = B * H * N * N * 2
+        res["steps_run_each"] = args.warmup + args.steps
+        rows.append(res)
+        log(f"[bench] contrast {res}")
+        del q, k, v, do, q3, k3, v3, do3
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "standard_contrast", "B": B, "H": H, "d": d, "dtype": "bf16", "causal": False,
+                      "rows": rows}), flush=True)
+
+
 def scaling_main(args, dev):
     """One head count, growing N: B=1, H=16, d=64, bf16, non-causal, N = 2K,
     4K, 8K, 16K, 32K.  Each N has its own grid size, so a rocprofv3 counter
@@ -720,6 +788,11 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed "
                          "(reported as graph_ms_per_step; value stays the eager step)")
+    ap.add_argument("--standard-contrast", action="store_true",
+                    help="instead of the headline line, time standard attention (every N x N matrix "
+                         "in HBM, plain torch products) next to this library's step, N = 2K-8K")
+    ap.add_argument("--contrast-n", type=int, default=0,
+                    help="with --standard-contrast: only this N (for a counter run per N)")
     ap.add_argument("--scaling", action="store_true",
                     help="instead of the headline line, time fwd+bwd at B=1, H=16, d=64 bf16, "
                          "non-causal, N = 2K..32K (for HBM-byte scaling under rocprofv3 counters)")
@@ -760,6 +833,8 @@ def main():
         return tile_sweep_main(args, dev)
     if args.ring:
         return ring_main(args, dev)
+    if args.standard_contrast:
+        return standard_contrast_main(args, dev)
     if args.scaling:
         return scaling_main(args, dev)
     if not w.backward:
