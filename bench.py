@@ -388,14 +388,20 @@ def time_attention(args, w, dev, steps, warmup):
     time_attention.extra_warmup = extra
     log(f"[bench] warmup {warmup} steps (+{extra} to reach {MIN_WARMUP_S} s) done")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(warmup + i, events[i])
+        step(warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
+    # The per-launch breakdown: as many steps again, with HIP events between
+    # the launches.  Kept out of the timed region above: at the small
+    # problems the events themselves add ~10 us to a step.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(warmup + steps + i, events[i])
+    torch.cuda.synchronize()
     per = {"fwd": [e[0].elapsed_time(e[1]) for e in events],
            "bwd_dq": [e[1].elapsed_time(e[2]) for e in events],
            "bwd_main": [e[2].elapsed_time(e[3]) for e in events]}
