@@ -411,6 +411,25 @@ def time_attention(args, w, dev, steps, warmup):
     log(f"[bench] timed {steps} steps: {ms_step:.3f} ms/step; fwd {fwd_ms:.3f} ms, "
         f"bwd dq (with the preprocessing) {dq_ms:.3f} / main {main_ms:.3f} ms")
 
+    if getattr(args, "cold", False):
+        # Cold caches: before each of K more steps, 512 MiB written to a
+        # scratch buffer (twice the 256 MB MALL, far more than the L2s), so
+        # the step finds none of its inputs cached.  Events around each step
+        # only, so the flush is not timed.
+        flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+        cold = []
+        for i in range(steps):
+            flush.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(warmup + 2 * steps + i)
+            e1.record(stream)
+            cold.append((e0, e1))
+        torch.cuda.synchronize()
+        time_attention.cold_ms = float(np.mean([a.elapsed_time(b) for a, b in cold]))
+        del flush
+        log(f"[bench] cold caches: {time_attention.cold_ms:.3f} ms/step")
+
     if getattr(args, "graph", False):
         # The same step recorded once into a HIP graph and replayed: what the
         # four launches cost without the host's per-launch work.  Eager and
@@ -791,6 +810,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line, print the metric's N=1K-16K sweep "
                          "(bf16, d=64, H=16, B=16384/N, causal and not) as one JSON line")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps that each follow a 512 MiB write (no input left in "
+                         "the L2s or the MALL; reported as cold_ms_per_step; value stays warm)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed "
                          "(reported as graph_ms_per_step; value stays the eager step)")
@@ -907,6 +929,9 @@ def main():
         "kernel_ms": {"fwd": round(fwd_ms, 4), "bwd_main": round(main_ms, 4),
                       "bwd_dq": round(dq_ms, 4)},
         **time_attention.spread,
+        **({"cold_ms_per_step": round(time_attention.cold_ms, 4),
+            "cold_tflops": round(f_step / (time_attention.cold_ms * 1e-3) / 1e12, 3)}
+           if getattr(args, "cold", False) else {}),
         "roofline": {"kernel": name, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "flops_per_launch": alg_flops,
