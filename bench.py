@@ -209,6 +209,33 @@ def calibration_copy(args, dev):
     del src, dst
 
 
+def compulsory_bytes(w, kernel):
+    """Bytes a kernel must move at least (each input read once, each output
+    written once), for the whole launch: the forward reads Q, K, V and writes
+    O and the LSE; the dK/dV pass reads Q, K, V, dO and two floats per query
+    row and writes dK, dV; the dQ pass (with the preprocessing of its rows)
+    reads Q, K, V, dO, O and the LSE and writes dQ and two floats per row."""
+    e = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    bh = w.B * w.H
+    q_side, k_side = bh * w.N * w.d * e, bh * w.Nk * w.d * e
+    rows = bh * w.N
+    if kernel == "fwd_kernel":
+        return 2 * q_side + 2 * k_side + 4 * rows
+    if kernel == "bwd_main_kernel":
+        return 2 * q_side + 4 * k_side + 8 * rows
+    return 4 * q_side + 2 * k_side + 12 * rows
+
+
+def attainable(flops, nbytes, peak_tflops, achieved_tflops):
+    """The attainable rate min(MFMA peak, AI x HBM bandwidth) for the kernel's
+    arithmetic intensity AI = algorithmic FLOPs / compulsory bytes, and the
+    achieved rate as a fraction of it."""
+    ai = flops / nbytes
+    att = min(peak_tflops, ai * HBM_PEAK_GBS / 1e3)
+    return {"arithmetic_intensity": round(ai, 1), "attainable": round(att, 1),
+            "frac_of_attainable": round(achieved_tflops / att, 4)}
+
+
 def gemm_reference(dtype, dev, n=8192, iters=20):
     """TFLOP/s of a plain n^3 matrix product in `dtype` through torch.matmul
     (the vendor GEMM library) on standard-normal operands, timed right after
@@ -935,7 +962,8 @@ def main():
         "roofline": {"kernel": name, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "flops_per_launch": alg_flops,
-                     "avg_launch_ms": round(dur_ms, 4)},
+                     "avg_launch_ms": round(dur_ms, 4),
+                     **attainable(alg_flops, compulsory_bytes(w, name), peak, achieved)},
     }
     if not args.no_gemm_reference:
         ref = gemm_reference(w.dtype, dev)
