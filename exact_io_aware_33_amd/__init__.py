@@ -29,7 +29,7 @@ __all__ = ["fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv", "fa_fwd_splitkv_num
            "fa_fwd_splitkv_workspace_bytes", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_ex",
            "fa_bwd_noalloc", "fa_merge_partials",
            "fa_bwd_workspace_bytes", "fa_softmax_rows", "fa_layernorm_rows", "fa_group_norm",
-           "FaError", "library_path", "load_library",
+           "attention", "FaError", "library_path", "load_library",
            "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_DQ", "FA_BWD_ALL"]
 
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_DQ, FA_BWD_ALL = (_lib.FA_BWD_PRE, _lib.FA_BWD_MAIN,
@@ -398,3 +398,50 @@ def fa_group_norm(x, groups, gamma=None, beta=None, *, eps=1e-5):
     x2 = x.contiguous().view(N * groups, (C // groups) * S)
     y, mean, rstd = fa_layernorm_rows(x2, gamma, beta, eps=eps, groups=groups, inner=S)
     return y.view(x.shape), mean.view(N, groups), rstd.view(N, groups)
+
+
+class _Attention(torch.autograd.Function):
+    """fa_fwd / fa_fwd_blocksparse forward, fa_bwd / fa_bwd_blocksparse
+    backward; saves Q, K, V, O and the LSE (O(N) beyond the inputs), nothing
+    of size N x N."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale, causal, key_lens, block_mask, mask_block, dropout_p, dropout_seed,
+                dropout_offset):
+        dr = dict(dropout_p=dropout_p, dropout_seed=dropout_seed, dropout_offset=dropout_offset)
+        if block_mask is None:
+            o, lse = fa_fwd(q, k, v, scale=scale, causal=causal, key_lens=key_lens, **dr)
+        else:
+            o, lse = fa_fwd_blocksparse(q, k, v, block_mask, mask_block=mask_block, scale=scale,
+                                        causal=causal, key_lens=key_lens, **dr)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (scale, causal, key_lens, block_mask, mask_block, dr)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        scale, causal, key_lens, block_mask, mask_block, dr = ctx.args
+        if do.stride() != o.stride() or do.dtype != o.dtype:  # dO in O's layout
+            do = torch.empty_strided(o.shape, o.stride(), dtype=o.dtype, device=o.device).copy_(do)
+        if block_mask is None:
+            dq, dk, dv = fa_bwd(q, k, v, o, lse, do, scale=scale, causal=causal, key_lens=key_lens, **dr)
+        else:
+            dq, dk, dv = fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, mask_block=mask_block,
+                                            scale=scale, causal=causal, key_lens=key_lens, **dr)
+        return dq, dk, dv, None, None, None, None, None, None, None, None
+
+
+def attention(q, k, v, *, scale=None, causal=False, key_lens=None, block_mask=None, mask_block=128,
+              dropout_p=0.0, dropout_seed=None, dropout_offset=0):
+    """O = softmax(scale Q K^T [+ masks]) V as a differentiable torch op:
+    the forward calls fa_fwd (fa_fwd_blocksparse with a block mask), the
+    backward fa_bwd (fa_bwd_blocksparse) with the saved O and LSE.  With
+    dropout and no seed given, a 64-bit seed is drawn from torch's default
+    CPU generator (so torch.manual_seed makes it reproducible); the backward
+    regenerates the same keep mask.  Tensors as for fa_fwd; dO is copied
+    into O's layout if it has another."""
+    if dropout_p > 0.0 and dropout_seed is None:
+        dropout_seed = int(torch.randint(0, 2 ** 62, (1,)).item())
+    return _Attention.apply(q, k, v, scale, causal, key_lens, block_mask, mask_block, dropout_p,
+                            dropout_seed or 0, dropout_offset)
