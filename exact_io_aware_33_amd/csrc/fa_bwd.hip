@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   const int Nq = p.Nq, Nk = p.Nk;
   const int nkt = (Nk + C::BKC - 1) / C::BKC;
   int bh, kt;  // causal: key tile 0 sees the most queries, so rank = kt is longest first
-  tile_of(blockIdx.x, gridDim.x, nkt, CAUSAL, bh, kt);
+  tile_of(blockIdx.x, gridDim.x, nkt, CAUSAL, p.cu_fill, bh, kt);
   const int b = bh / p.H, hh = bh - b * p.H;
   const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;     // Q, dO
   const int64_t kbase = (int64_t)b * p.ksb + (int64_t)hh * p.ksh;  // K, V, dK, dV
@@ -679,7 +679,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   const int Nq = p.Nq, Nk = p.Nk;
   const int nqt = (Nq + C::BR - 1) / C::BR;
   int bh, qt;
-  tile_of(blockIdx.x, gridDim.x, nqt, CAUSAL, bh, qt);
+  tile_of(blockIdx.x, gridDim.x, nqt, CAUSAL, p.cu_fill, bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int b = bh / p.H, hh = bh - b * p.H;
   const int64_t base = (int64_t)b * p.sb + (int64_t)hh * p.sh;     // Q, dO, dQ
@@ -1092,10 +1092,12 @@ static hipError_t launch_main_t(const AttnParams &p, hipStream_t s) {
   using C = BwdCfg<T, D>;
   const int64_t nkt = (p.Nk + C::BKC - 1) / C::BKC;
   const int64_t grid = (int64_t)p.B * p.H * nkt;
+  const void *fn = reinterpret_cast<const void *>(&bwd_main_kernel<T, D, CAUSAL, SPARSE, DROP>);
+  static const int fill = resident_per_cu(fn, 256);
   AttnParams a = p;
+  a.cu_fill = fill;
   void *args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_main_kernel<T, D, CAUSAL, SPARSE, DROP>),
-                         dim3((unsigned)grid), dim3(256), args, 0, s);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
@@ -1103,10 +1105,12 @@ static hipError_t launch_dq_t(const AttnParams &p, hipStream_t s) {
   using C = DqCfg<T, D>;
   const int64_t nqt = (p.Nq + C::BR - 1) / C::BR;
   const int64_t grid = (int64_t)p.B * p.H * nqt;
+  const void *fn = reinterpret_cast<const void *>(&bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP>);
+  static const int fill = resident_per_cu(fn, 256);
   AttnParams a = p;
+  a.cu_fill = fill;
   void *args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP>),
-                         dim3((unsigned)grid), dim3(256), args, 0, s);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
 template <typename T, int D, bool DROP>

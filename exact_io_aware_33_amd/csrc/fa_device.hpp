@@ -306,8 +306,20 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 // head (16K keys, d = 64) their K and V no longer fit the XCD's 4 MB L2
 // together, HBM reads grew 1.6-2x for a 1.4% faster step, so long sequences
 // stay head by head.
-__device__ __forceinline__ void tile_of(int id, int total, int ntile, bool rank_major, int &bh,
-                                        int &rank) {
+//
+// The first `fill` passes of kCuPerXcd slots (fill = workgroups resident per
+// CU) deal the longest-first list in alternating direction; later slots keep
+// it in order.  An XCD places its first workgroups one per CU and then a
+// second, third ... on each CU in the same order, so CU c starts with list
+// positions c, 2 kCuPerXcd - 1 - c, 2 kCuPerXcd + c, ...: a long tile beside
+// a short one.  A CU issues its oldest wavefronts first, so the workgroups
+// sharing it run nearly one after another, and when the whole launch is
+// resident at once (small problems) it ends with the CU whose tiles add up to
+// the most work.  Later workgroups start as slots free up, longest first.
+// Any order is correct; this one only balances the CUs.
+constexpr int kCuPerXcd = 32;
+__device__ __forceinline__ void tile_of(int id, int total, int ntile, bool rank_major, int fill,
+                                        int &bh, int &rank) {
   constexpr int kXcd = 8;
   const int nbh = total / ntile;
   if (nbh % kXcd == 0) {
@@ -315,8 +327,12 @@ __device__ __forceinline__ void tile_of(int id, int total, int ntile, bool rank_
     const int xcd = id % kXcd, slot = id / kXcd;
     int j;
     if (rank_major && ntile <= 64) {
-      j = slot % hpx;
-      rank = slot / hpx;
+      const int n = hpx * ntile;  // this XCD's slots
+      const int pass = slot / kCuPerXcd, pos = slot - pass * kCuPerXcd;
+      const int len = min(kCuPerXcd, n - pass * kCuPerXcd);
+      const int q = pass * kCuPerXcd + ((pass & 1) && pass < fill ? len - 1 - pos : pos);
+      j = q % hpx;
+      rank = q / hpx;
     } else {
       j = slot / ntile;
       rank = slot - j * ntile;

@@ -135,7 +135,7 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
     bh = logical / nqt;
     qt = logical - bh * nqt;
   } else {
-    tile_of(blockIdx.x, gridDim.x, nqt, CAUSAL, bh, qt);
+    tile_of(blockIdx.x, gridDim.x, nqt, CAUSAL, p.cu_fill, bh, qt);
   }
   if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
   const int b = bh / p.H, hh = bh - b * p.H;
@@ -745,10 +745,12 @@ static hipError_t launch_fwd_t(const AttnParams &p, hipStream_t s) {
   using C = FwdCfg<T, D, SPARSE, W>;
   const int64_t nqt = (p.Nq + C::BR - 1) / C::BR;
   const int64_t grid = (int64_t)p.B * p.H * nqt * (SPLIT ? p.nsplit : 1);
+  const void *fn = reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE, DROP, SPLIT, W>);
+  static const int fill = resident_per_cu(fn, C::NTHR);
   AttnParams a = p;
+  a.cu_fill = fill;
   void *args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<T, D, CAUSAL, SPARSE, DROP, SPLIT, W>),
-                         dim3((unsigned)grid), dim3(C::NTHR), args, 0, s);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(C::NTHR), args, 0, s);
 }
 
 template <typename T, int D, bool DROP, int W>

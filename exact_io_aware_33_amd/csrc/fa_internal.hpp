@@ -52,7 +52,19 @@ struct AttnParams {
   // the preprocessing kernel's arithmetic) and writes them to the workspace,
   // instead of reading what the preprocessing kernel wrote
   int32_t dq_pre;
+  // workgroups of the launched kernel resident on one CU at a time (set by
+  // the launcher from the occupancy query): tile_of deals the first that many
+  // passes of each XCD's tile list in alternating direction
+  int32_t cu_fill;
 };
+
+// Workgroups of kernel `fn` (`threads` per workgroup, static LDS only) that one
+// CU holds at a time, queried once per kernel; 1 if the query fails.
+inline int resident_per_cu(const void *fn, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess || n < 1) n = 1;
+  return n;
+}
 
 // Merge of partial results over disjoint key sets (fa_merge.hip): part s is
 // (o_parts[s], lse_parts[s]); O and every O_s share the strides (sb, sh, sn).

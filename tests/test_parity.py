@@ -183,11 +183,16 @@ def test_blocksparse_small(dtype, d, causal, mb):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("B,H,N,d,lens", [(2, 4, 1024, 64, None), (1, 8, 2048, 64, None),
-                                          (2, 8, 640, 128, (1, 640)), (1, 8, 4096, 64, None)])
+                                          (2, 8, 640, 128, (1, 640)), (1, 8, 4096, 64, None),
+                                          (2, 12, 1536, 64, None), (1, 24, 2048, 64, (1, 2048)),
+                                          (4, 16, 1024, 64, None)])
 def test_causal_rank_major_tile_order(dtype, B, H, N, d, lens):
     """Causal launches whose heads split evenly over the 8 XCDs and that have
     at most 64 tiles per head are issued rank-major (longest tiles of every
-    head first): every (head, tile) must still be computed exactly once."""
+    head first), the first passes of 32 slots of each XCD dealt in
+    alternating direction (36, 48 and 64 slots per XCD here: a partial
+    reversed pass, a full one): every (head, tile) must still be computed
+    exactly once."""
     check_case(B, H, N, d, dtype, causal=True, lens=lens, seed=3)
 
 
