@@ -58,7 +58,10 @@
  *   (H*N*d, N*d, d); a [B, N, H, d] array has (N*H*d, d, H*d).
  * Memory.  Every data pointer is a DEVICE pointer owned by the caller; the
  *   library never allocates, frees or keeps device memory between calls and
- *   holds no state, so concurrent calls on different streams are safe.
+ *   holds no state, so concurrent calls on different streams are safe.  (The
+ *   first launch of each kernel variant in a process also asks the runtime,
+ *   once, how many of its workgroups one CU holds: a host-side query that
+ *   enqueues nothing, used only to order the tiles.)
  * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *   enqueue work and return; the caller synchronises before reading results
  *   and keeps every buffer alive until then.
