@@ -468,7 +468,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     commit(i + C::AHEAD);
     sync_ring();
   };
-  // Iteration i for an unmasked block i with a successor, as one sequence of
+  // Iteration i for an unmasked block i, as one sequence of
   // MFMA groups (NGA score / dP MFMAs of block i+1, then NGB dV / dK MFMAs of
   // block i), each paired with a slice of the vector work of block i:
   //  during the score MFMAs: P, dS of the first 8 rows (register order), then
@@ -478,7 +478,10 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
   // Operand reads run two groups ahead of their MFMA; the next block's
   // LDS-DMA is spread over the first groups.  `par` is i mod NSLOT (a
   // compile-time constant in the unrolled loop, so every LDS address is a
-  // loop-invariant register plus an immediate).
+  // loop-invariant register plus an immediate).  For the last block the
+  // next-block products are computed on the repeated last block (the ring
+  // fetches it again past the end) and never used, as in the generic
+  // iteration.
   // With DROP, KX holds the keep bytes of block i (its dP MFMAs started from
   // 0, -D enters per row as in softmax_grad) and the generator rounds for
   // block i+1's bytes (into KY) ride one per MFMA group.
@@ -514,7 +517,7 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
         if (grp == kPhiloxRounds - 1) keep_finish_key_col(KY, lane);
       }
     };
-    if constexpr (DROP) keep_ctr_key_col(KY, p, bh, qblock_start(i + 1), key, lane);
+    if constexpr (DROP) keep_ctr_key_col(KY, p, bh, qblock_start(min(i + 1, nq - 1)), key, lane);
     // ---- score / dP MFMAs of block i+1
     frag af[3];
     af[0] = qfrag(qn, sdp_order(0));
@@ -614,15 +617,15 @@ __global__ void __launch_bounds__(256) bwd_main_kernel(AttnParams p) {
     using s2 = std::integral_constant<int, 2>;
     using s3 = std::integral_constant<int, 3>;
     uint32_t KA[4], KB[4];  // keep bytes of the current / next block (DROP)
-    if (DROP && i + C::NSLOT < nq) keep_bytes_key_col(KA, p, bh, qblock_start(i), key, lane);
-    for (; i + C::NSLOT < nq; i += C::NSLOT) {
+    if (DROP && i + C::NSLOT <= nq) keep_bytes_key_col(KA, p, bh, qblock_start(i), key, lane);
+    for (; i + C::NSLOT <= nq; i += C::NSLOT) {
       iter_steady(i, s0{}, SA, DA, SB, DB, KA, KB);
       iter_steady(i + 1, s1{}, SB, DB, SA, DA, KB, KA);
       iter_steady(i + 2, s2{}, SA, DA, SB, DB, KA, KB);
       iter_steady(i + 3, s3{}, SB, DB, SA, DA, KB, KA);
     }
   }
-  // the rest: unmasked blocks (with dropout: every block past the masked ones)
+  // the rest: fewer than NSLOT unmasked blocks
   for (; i < nq; ++i) {
     iter_any(i, ffalse{}, SA, DA, SB, DB);
     swap_ab();
