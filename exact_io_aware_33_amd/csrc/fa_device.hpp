@@ -283,7 +283,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // XCD receives a contiguous range of logical ids (consecutive tiles of the same
 // (batch, head), which then share K/V in that XCD's L2).  Bijective for any
 // grid size; correctness does not depend on the dispatch order.
-__device__ __forceinline__ int xcd_remap(int id, int total) {
+__host__ __device__ __forceinline__ int xcd_remap(int id, int total) {
   constexpr int kXcd = 8;
   const int per = total / kXcd, rem = total % kXcd;
   const int xcd = id % kXcd, slot = id / kXcd;
@@ -318,8 +318,8 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 // the most work.  Later workgroups start as slots free up, longest first.
 // Any order is correct; this one only balances the CUs.
 constexpr int kCuPerXcd = 32;
-__device__ __forceinline__ void tile_of(int id, int total, int ntile, bool rank_major, int fill,
-                                        int &bh, int &rank) {
+__host__ __device__ __forceinline__ void tile_of(int id, int total, int ntile, bool rank_major,
+                                                 int fill, int &bh, int &rank) {
   constexpr int kXcd = 8;
   const int nbh = total / ntile;
   if (nbh % kXcd == 0) {
@@ -329,7 +329,7 @@ __device__ __forceinline__ void tile_of(int id, int total, int ntile, bool rank_
     if (rank_major && ntile <= 64) {
       const int n = hpx * ntile;  // this XCD's slots
       const int pass = slot / kCuPerXcd, pos = slot - pass * kCuPerXcd;
-      const int len = min(kCuPerXcd, n - pass * kCuPerXcd);
+      const int len = n - pass * kCuPerXcd < kCuPerXcd ? n - pass * kCuPerXcd : kCuPerXcd;
       const int q = pass * kCuPerXcd + ((pass & 1) && pass < fill ? len - 1 - pos : pos);
       j = q % hpx;
       rank = q / hpx;
