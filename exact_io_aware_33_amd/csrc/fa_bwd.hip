@@ -957,7 +957,8 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
     commit(j + C::AHEAD);
     sync_ring();
   };
-  // Iteration j for an unmasked tile j with a successor: the NGA score / dP
+  // Iteration j for an unmasked tile j (its successor may be masked, or past
+  // the end the repeated last tile, whose products go unused): the NGA score / dP
   // MFMAs of tile j+1 carry dS of the first 8 rows of tile j (then the
   // packing of step 0), the first half of the NGB dQ MFMAs carry the last 8
   // rows; operand reads two groups ahead; the next tile's LDS-DMA spread over
@@ -981,7 +982,7 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
         if (grp == kPhiloxRounds - 1) keep_finish_query_col(KY, lane);
       }
     };
-    if constexpr (DROP) keep_ctr_query_col(KY, p, bh, qi, tile_start(j + 1), lane);
+    if constexpr (DROP) keep_ctr_query_col(KY, p, bh, qi, tile_start(min(j + 1, ntiles - 1)), lane);
     frag af[3];
     af[0] = kvfrag(kn, 0);
     af[1] = kvfrag(kn, 1);
@@ -1047,7 +1048,10 @@ __global__ void __launch_bounds__(256, (D == 128 ? 2 : 1)) bwd_dq_kernel(AttnPar
   using s2 = std::integral_constant<int, 2>;
   using s3 = std::integral_constant<int, 3>;
   {
-    const int j_steady = min(n_full, ntiles - 1);  // tile j unmasked, j+1 exists
+    // tile j unmasked; its successor is a masked tile or, past the end, the
+    // last tile again (the ring fetches it once more), whose products are
+    // never used
+    const int j_steady = n_full;
     uint32_t KA[4], KB[4];  // keep bytes of the current / next tile (DROP)
     if (DROP && j + C::NSLOT <= j_steady) keep_bytes_query_col(KA, p, bh, qi, tile_start(j), lane);
     for (; j + C::NSLOT <= j_steady; j += C::NSLOT) {
