@@ -613,7 +613,10 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
     rotate();
   }
   {
-    const int j_steady = min(n_full, ntiles) - 1;  // tiles j and j+1 unmasked
+    // tiles j and j+1 unmasked; when no tile is masked, also the last tile,
+    // whose successor is the last tile again (the ring fetches it once more:
+    // its scores only ever raise the reference point to a max already seen)
+    const int j_steady = n_full >= ntiles ? ntiles : n_full - 1;
     // Two iterations per trip restore the roles at the loop back edge, so the
     // steady loop needs no register copies.
     using odd = std::integral_constant<int, 1>;
