@@ -372,7 +372,9 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
     }
   };
   // steps 2-3 for the scores in S: the row max over both half-waves (four
-  // independent max chains), scaled by scale*log2(e).  The reference point
+  // independent max chains, IEEE maximum: a NaN score propagates, and no
+  // NaN-quieting instruction precedes each max as for maxNum), scaled by
+  // scale*log2(e).  The reference point
   // moves only when some lane's max passed it by more than the slack; then
   // the carried state -- O, the partial sums and the exponentials P of the
   // previous tile, not yet added to O -- is rescaled by exp2(old - new).
@@ -383,9 +385,10 @@ __global__ void __launch_bounds__((FwdCfg<T, D, SPARSE, W>::NTHR), (D == 64 ? (D
     for (int qb = 0; qb < QB; ++qb) {
       float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int e = 0; e < NSB * 16; ++e) mx[e & 3] = fmaxf(mx[e & 3], EL(S, qb * NSB * 16 + e));
-      float m = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-      m = fmaxf(m, xor32(m));
+      for (int e = 0; e < NSB * 16; ++e) mx[e & 3] = __builtin_elementwise_maximum(mx[e & 3], EL(S, qb * NSB * 16 + e));
+      float m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx[0], mx[1]),
+                                              __builtin_elementwise_maximum(mx[2], mx[3]));
+      m = __builtin_elementwise_maximum(m, xor32(m));
       mt[qb] = (decltype(masked)::value && m == -INFINITY) ? -INFINITY : m * c2;
       grow = grow || mt[qb] > m_run[qb] + kMaxSlack;
     }
