@@ -130,8 +130,11 @@ MODES = {
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mode", list(MODES))
-@pytest.mark.parametrize("N", [1, 77, 128, 300])
+@pytest.mark.parametrize("N", [1, 77, 128, 192, 256, 300, 320])
 def test_forward_backward_small(dtype, d, mode, N):
+    """Every mode at lengths below one tile, at whole tiles (2, 3, 4 and 5
+    tiles of 64 keys: the pipelined iterations then run up to the last tile)
+    and with a ragged tail."""
     kw = dict(MODES[mode])
     if "lens" in kw:
         kw["lens"] = (1, max(1, N))
